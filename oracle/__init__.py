@@ -1,0 +1,22 @@
+"""CPU fp64 oracle for cross-layer shared-KV attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this package:
+only the tests, the smoke check and the benchmark's CPU-baseline leg call it.
+It shares no code with the HIP library (no kernels, headers, helpers or
+constant tables); both sides only consume the seeded tensors of ``datagen``.
+
+The oracle computes the plain definitions, in float64, from logical
+(unpaged) tensors:
+
+* ``attention``  -- effective K/V of a layer through an explicit layer->source
+                    map, single-query decode attention, causal / non-causal
+                    prefill attention, and the factorized (basis + low-rank
+                    int8 residual) key/value reconstruction.
+* ``plan``       -- which layers own cached K/V, the owner-slot numbering and
+                    the validity rules of a sharing map.
+
+Every function is pinned by the CPU tests to something other than itself
+(closed forms, a library routine, invariants, brute force); none is marked
+"parity unpinned".
+"""
+from . import attention, plan  # noqa: F401
