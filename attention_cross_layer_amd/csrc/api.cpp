@@ -1,0 +1,157 @@
+// C ABI glue: host-side argument validation (before any HIP call) and the
+// dispatch to the gfx950 launchers.  Pure C++; the launchers live in the .hip
+// files.
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "internal.h"
+
+using namespace kvs;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+kvs_status check_layer(const kvs_plan* plan, int32_t layer) {
+  if (!plan) return fail(KVS_ERR_ARG, "null plan");
+  if (layer < 0 || layer >= plan->p.cfg.n_layers) return fail(KVS_ERR_ARG, "layer out of range");
+  return KVS_OK;
+}
+
+kvs_status check_batch(const kvs_plan* plan, int32_t batch) {
+  if (batch < 1 || batch > plan->p.cfg.max_batch) return fail(KVS_ERR_RANGE, "batch out of range");
+  return KVS_OK;
+}
+
+kvs_status hip_status(int err, const char* what) {
+  if (err == 0) return KVS_OK;
+  return fail(KVS_ERR_HIP, std::string(what) + ": " + hip_error_name(err));
+}
+
+float scale_log2(int32_t hd) { return (float)(1.4426950408889634 / std::sqrt((double)hd)); }
+
+}  // namespace
+
+extern "C" kvs_status kvs_append(const kvs_plan* plan, const kvs_cache* cache, int32_t layer,
+                                 const void* k, const void* v, int32_t n,
+                                 const int32_t* start_pos, int32_t batch, void* stream) {
+  clear_error();
+  kvs_status st = check_layer(plan, layer);
+  if (st != KVS_OK) return st;
+  const Plan& p = plan->p;
+  if (p.cfg.kind != KVS_DENSE) return fail(KVS_ERR_ARG, "kvs_append needs a dense plan");
+  if (!cache || !k || !v || !start_pos || !cache->k_pool || !cache->v_pool || !cache->page_table)
+    return fail(KVS_ERR_ARG, "null argument");
+  if ((st = check_batch(plan, batch)) != KVS_OK) return st;
+  if (n < 0 || n > p.cfg.max_ctx) return fail(KVS_ERR_RANGE, "n out of range");
+  if (!p.layers[layer].owns_kv)
+    return fail(KVS_ERR_NOT_SOURCE, "layer " + std::to_string(layer) + " owns no cache entries");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(cache->k_pool) || !aligned16(cache->v_pool))
+    return fail(KVS_ERR_ALIGN, "k, v and the pools must be 16-byte aligned");
+  if (!aligned4(start_pos) || !aligned4(cache->page_table)) return fail(KVS_ERR_ALIGN, "misaligned int32 array");
+  if (n == 0) return KVS_OK;
+  AppendLaunch a;
+  a.k_pool = cache->k_pool;
+  a.v_pool = cache->v_pool;
+  a.page_table = cache->page_table;
+  a.pages_per_seq = p.pages_per_seq;
+  a.n_phys_pages = p.n_phys_pages;
+  a.n_kv_heads = p.cfg.n_kv_heads;
+  a.head_dim = p.cfg.head_dim;
+  a.dtype = p.cfg.dtype;
+  a.slot_offset = (int64_t)p.layers[layer].src_slot[0] * p.n_phys_pages * p.cfg.n_kv_heads * kPage *
+                  p.cfg.head_dim;
+  a.k = k;
+  a.v = v;
+  a.n = n;
+  a.start_pos = start_pos;
+  a.batch = batch;
+  a.max_ctx = p.cfg.max_ctx;
+  return hip_status(launch_append(a, stream), "append launch");
+}
+
+extern "C" kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cache, int32_t layer,
+                                      const void* q, const int32_t* seq_len, int32_t batch,
+                                      int32_t max_seq_len, int32_t n_splits, void* out,
+                                      int32_t out_dtype, void* workspace, size_t ws_bytes,
+                                      void* stream) {
+  clear_error();
+  kvs_status st = check_layer(plan, layer);
+  if (st != KVS_OK) return st;
+  const Plan& p = plan->p;
+  if (!cache || !q || !seq_len || !out || !workspace) return fail(KVS_ERR_ARG, "null argument");
+  if ((st = check_batch(plan, batch)) != KVS_OK) return st;
+  if (out_dtype != KVS_F32 && out_dtype != KVS_BF16) return fail(KVS_ERR_ARG, "bad out_dtype");
+  if (n_splits == 0) {
+    if ((st = kvs_decode_splits(plan, batch, max_seq_len, &n_splits)) != KVS_OK) return st;
+  }
+  size_t need = 0;
+  if ((st = kvs_decode_workspace_size(plan, batch, n_splits, &need)) != KVS_OK) return st;
+  if (ws_bytes < need) return fail(KVS_ERR_RANGE, "workspace too small: need " + std::to_string(need));
+  if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) || !aligned4(seq_len))
+    return fail(KVS_ERR_ALIGN, "q, out and workspace must be 16-byte aligned");
+  const kvs_layer_info& li = p.layers[layer];
+  const int32_t group = p.cfg.n_q_heads / p.cfg.n_kv_heads;
+  if (p.cfg.kind == KVS_FACTORIZED) return fail(KVS_ERR_UNSUPPORTED, "factorized decode is not built");
+  if (!cache->k_pool || !cache->v_pool || !cache->page_table) return fail(KVS_ERR_ARG, "null cache pool");
+  if (!aligned16(cache->k_pool) || !aligned16(cache->v_pool) || !aligned4(cache->page_table))
+    return fail(KVS_ERR_ALIGN, "pools must be 16-byte aligned");
+  DecodeLaunch a;
+  a.k_pool = cache->k_pool;
+  a.v_pool = cache->v_pool;
+  a.page_table = cache->page_table;
+  a.pages_per_seq = p.pages_per_seq;
+  a.n_phys_pages = p.n_phys_pages;
+  a.n_kv_heads = p.cfg.n_kv_heads;
+  a.n_q_heads = p.cfg.n_q_heads;
+  a.head_dim = p.cfg.head_dim;
+  a.group = group;
+  a.dtype = p.cfg.dtype;
+  a.slot_stride = (int64_t)p.n_phys_pages * p.cfg.n_kv_heads * kPage * p.cfg.head_dim;
+  a.n_src = li.n_src;
+  a.slot[0] = li.src_slot[0];
+  a.slot[1] = li.src_slot[1];
+  a.weight[0] = li.weight[0];
+  a.weight[1] = li.weight[1];
+  a.q = q;
+  a.seq_len = seq_len;
+  a.max_ctx = p.cfg.max_ctx;
+  a.batch = batch;
+  a.n_splits = n_splits;
+  a.scale_log2 = scale_log2(p.cfg.head_dim);
+  a.ws = static_cast<float*>(workspace);
+  a.out = out;
+  a.out_dtype = out_dtype;
+  return hip_status(launch_decode(a, stream), "decode launch");
+}
+
+extern "C" kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cache* cache,
+                                             int32_t layer, const void* q, int32_t n,
+                                             const int32_t* seq_len, int32_t batch, int32_t causal,
+                                             void* out, int32_t out_dtype, void* stream) {
+  clear_error();
+  kvs_status st = check_layer(plan, layer);
+  if (st != KVS_OK) return st;
+  (void)cache; (void)q; (void)n; (void)seq_len; (void)batch; (void)causal; (void)out;
+  (void)out_dtype; (void)stream;
+  return fail(KVS_ERR_UNSUPPORTED, "prefill is not built");
+}
+
+extern "C" kvs_status kvs_append_factorized(const kvs_plan* plan, const kvs_cache* cache,
+                                            int32_t layer, const void* ck, const void* cv,
+                                            const int8_t* dk, const int8_t* dv, const void* sk,
+                                            const void* sv, const uint8_t* rank, int32_t n,
+                                            const int32_t* start_pos, int32_t batch, void* stream) {
+  clear_error();
+  kvs_status st = check_layer(plan, layer);
+  if (st != KVS_OK) return st;
+  (void)cache; (void)ck; (void)cv; (void)dk; (void)dv; (void)sk; (void)sv; (void)rank; (void)n;
+  (void)start_pos; (void)batch; (void)stream;
+  return fail(KVS_ERR_UNSUPPORTED, "factorized cache is not built");
+}
+
+namespace kvs {
+bool fact_shape_supported(int32_t, int32_t, int32_t, int32_t) { return false; }
+}  // namespace kvs

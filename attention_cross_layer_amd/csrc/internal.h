@@ -1,0 +1,169 @@
+// Library-internal declarations shared by the host planner, the ABI glue and
+// the HIP launchers.  Nothing here is exported.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "kvshare.h"
+
+namespace kvs {
+
+constexpr int kPage = 64;   // tokens per page == keys per decode tile
+
+struct Plan {
+  kvs_config cfg;
+  std::vector<kvs_layer_info> layers;
+  int32_t n_slots = 0;
+  int32_t last_owner = -1;
+  int32_t n_mixed = 0;
+  int32_t pages_per_seq = 0;
+  int32_t n_phys_pages = 0;
+};
+
+// thread-local error text
+kvs_status fail(kvs_status st, const std::string& msg);
+void clear_error();
+
+inline size_t elem_bytes(int32_t dtype) { return dtype == KVS_F32 ? 4 : 2; }
+
+// Whether the decode kernels are instantiated for this shape and source count.
+bool decode_shape_supported(int32_t dtype, int32_t head_dim, int32_t group, int32_t n_src);
+
+// ------------------------------------------------------------ HIP launchers
+// Implemented in the .hip files; each returns a hipError_t value (0 = ok).
+
+struct DecodeLaunch {
+  const void* k_pool;          // base of the K pool
+  const void* v_pool;
+  const int32_t* page_table;
+  int32_t pages_per_seq;
+  int32_t n_phys_pages;
+  int32_t n_kv_heads;
+  int32_t n_q_heads;
+  int32_t head_dim;
+  int32_t group;
+  int32_t dtype;
+  int64_t slot_stride;         // elements per slot
+  int32_t n_src;
+  int32_t slot[2];
+  float weight[2];
+  const void* q;
+  const int32_t* seq_len;
+  int32_t max_ctx;
+  int32_t batch;
+  int32_t n_splits;
+  float scale_log2;            // log2(e) / sqrt(hd)
+  float* ws;                   // workspace base
+  void* out;
+  int32_t out_dtype;
+};
+int launch_decode(const DecodeLaunch& a, void* stream);
+
+struct AppendLaunch {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* page_table;
+  int32_t pages_per_seq;
+  int32_t n_phys_pages;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;
+  int64_t slot_offset;         // elements to the layer's slot
+  const void* k;
+  const void* v;
+  int32_t n;
+  const int32_t* start_pos;
+  int32_t batch;
+  int32_t max_ctx;
+};
+int launch_append(const AppendLaunch& a, void* stream);
+
+struct PrefillLaunch {
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  int32_t pages_per_seq;
+  int32_t n_kv_heads;
+  int32_t n_q_heads;
+  int32_t head_dim;
+  int64_t slot_stride;
+  int32_t n_src;
+  int32_t slot[2];
+  float weight[2];
+  const void* q;
+  int32_t n;
+  const int32_t* seq_len;
+  int32_t max_ctx;
+  int32_t batch;
+  int32_t causal;
+  float scale_log2;
+  void* out;
+  int32_t out_dtype;
+};
+int launch_prefill(const PrefillLaunch& a, void* stream);
+
+struct FactAppendLaunch {
+  void* ck_pool; void* cv_pool;
+  void* dk_pool; void* dv_pool;
+  void* sk_pool; void* sv_pool;
+  void* rank_pool;
+  const int32_t* page_table;
+  int32_t pages_per_seq;
+  int32_t n_phys_pages;
+  int32_t n_kv_heads;
+  int32_t basis_rank;
+  int32_t resid_rank_max;
+  int32_t coef_slot;           // -1: no coefficient write
+  int32_t layer;
+  const void* ck; const void* cv;
+  const int8_t* dk; const int8_t* dv;
+  const void* sk; const void* sv;
+  const uint8_t* rank;
+  int32_t n;
+  const int32_t* start_pos;
+  int32_t batch;
+  int32_t max_ctx;
+};
+int launch_fact_append(const FactAppendLaunch& a, void* stream);
+
+struct FactDecodeLaunch {
+  const void* ck_pool; const void* cv_pool;
+  const void* dk_pool; const void* dv_pool;
+  const void* sk_pool; const void* sv_pool;
+  const void* rank_pool;
+  const void* basis_k; const void* basis_v;
+  const void* ubasis_k; const void* ubasis_v;
+  const int32_t* page_table;
+  int32_t pages_per_seq;
+  int32_t n_phys_pages;
+  int32_t n_kv_heads;
+  int32_t n_q_heads;
+  int32_t head_dim;
+  int32_t basis_rank;
+  int32_t resid_rank_max;
+  int32_t coef_slot;
+  int32_t layer;
+  const void* q;
+  const int32_t* seq_len;
+  int32_t max_ctx;
+  int32_t batch;
+  int32_t n_splits;
+  float scale_log2;
+  float* ws;
+  void* out;
+  int32_t out_dtype;
+};
+int launch_fact_decode(const FactDecodeLaunch& a, void* stream);
+bool fact_shape_supported(int32_t head_dim, int32_t group, int32_t basis_rank,
+                          int32_t resid_rank_max);
+
+const char* hip_error_name(int err);
+
+}  // namespace kvs
+
+struct kvs_plan {
+  kvs::Plan p;
+};

@@ -68,6 +68,7 @@ class Workload:
     basis_rank: int = 0
     resid_rank_max: int = 0
     rank16_frac: float = 0.0
+    dg_stride: int = 8         # depthgraft: layers >= 2*stride mix l-stride, l-2*stride
 
     @property
     def group(self) -> int:
@@ -126,8 +127,8 @@ def share_map(wl: Workload, device="cpu") -> Tuple[torch.Tensor, torch.Tensor]:
             w[l, 0] = 1.0
     elif wl.share == "depthgraft":
         a = torch.rand(L, generator=_gen(wl, TAG_MIX, 0, "cpu"), dtype=torch.float32)
-        n_own = 16 if L >= 24 else (2 * L) // 3
-        stride = n_own // 2
+        stride = wl.dg_stride
+        n_own = 2 * stride
         for l in range(L):
             if l < n_own:
                 src[l, 0] = l

@@ -1,0 +1,259 @@
+/*
+ * kvshare.h -- C ABI of a cross-layer shared-KV attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed.  GQA attention in which transformer layer l attends over
+ * the cached keys/values of the layer(s) a sharing map names for it:
+ *   - adjacent sharing (Cross-Layer Attention, "Reducing Transformer
+ *     Key-Value Cache Size with Cross-Layer Attention", Methodology and
+ *     Abstract: some layers compute K/V, the following ones reuse it);
+ *   - any "bottom" partitioning of the unified framework of "A Systematic
+ *     Study of Cross-Layer KV Sharing for Efficient LLM Inference" (TL;DR):
+ *     every source at or below its reader;
+ *   - two-source mixing (DepthGraft, "DepthGraft: Structural Regularization
+ *     through Hierarchical Cross-Layer KV Reconstruction", Abstract: deep-layer
+ *     K/V rebuilt from stride-aligned shallow/middle source pairs), read as
+ *     K~ = w1 K_s1 + w2 K_s2 (same weights for V);
+ *   - a factorized cache (DepthWeave-KV, "DepthWeave-KV: Smarter KV Cache
+ *     Compression by Sharing Across Layers and Adapting Per Token", Core
+ *     Mechanism and Framework Shift): K_l[t] = c[t] B_pair
+ *     + s_l[t] * sum_{j<r_t} d_l[t,j] U_l[j], V alike, c/B shared by a layer
+ *     pair, int8 codes d with an fp16 per-token scale s, rank r_t per token.
+ * Attention is softmax(q K~^T / sqrt(head_dim)) V~, query head h reading K/V
+ * head floor(h / (n_q_heads / n_kv_heads)).
+ *
+ * Conventions for every call.
+ *   - The library never allocates device memory and never creates streams.
+ *     All device buffers (cache pools, page table, queries, outputs,
+ *     workspace) are owned by the caller; sizes come from kvs_cache_layout()
+ *     and kvs_decode_workspace_size().
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Compute calls are asynchronous on that stream; device faults surface at
+ *     the caller's next synchronisation.
+ *   - Arguments are validated on the host before any HIP call; on error the
+ *     call returns a non-zero kvs_status, launches nothing, and
+ *     kvs_last_error() (thread-local) describes the problem.
+ *   - Device pointers to tensors must be 16-byte aligned (KVS_ERR_ALIGN).
+ *   - Tensors are dense and row-major in the shapes given.
+ *   - "bf16" data is passed as raw 16-bit bfloat16 patterns.
+ */
+#ifndef KVSHARE_H
+#define KVSHARE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define KVS_API __attribute__((visibility("default")))
+#else
+#define KVS_API
+#endif
+
+typedef enum {
+  KVS_OK = 0,
+  KVS_ERR_ARG = 1,          /* null pointer, size or enum out of range         */
+  KVS_ERR_MAP = 2,          /* malformed sharing map row                        */
+  KVS_ERR_NOT_SOURCE = 3,   /* map names a non-owner as source; append to a
+                               layer that owns no cache entries                 */
+  KVS_ERR_RANGE = 4,        /* count beyond cache capacity or workspace size    */
+  KVS_ERR_UNSUPPORTED = 5,  /* valid request this build does not implement
+                               (a source above its reader, an unsupported
+                               head_dim / group size / dtype combination)       */
+  KVS_ERR_ALIGN = 6,        /* a device pointer is not 16-byte aligned          */
+  KVS_ERR_HIP = 7           /* a HIP launch failed                              */
+} kvs_status;
+
+typedef enum { KVS_F32 = 0, KVS_BF16 = 1 } kvs_dtype;
+typedef enum { KVS_DENSE = 0, KVS_FACTORIZED = 1 } kvs_kind;
+
+/* Model and capacity description. */
+typedef struct {
+  int32_t n_layers;        /* L >= 1                                           */
+  int32_t n_q_heads;       /* Hq, multiple of n_kv_heads                        */
+  int32_t n_kv_heads;      /* Hkv                                               */
+  int32_t head_dim;        /* hd: 64 or 128                                     */
+  int32_t dtype;           /* kvs_dtype of the dense cache and the queries;
+                              the factorized cache is bf16                      */
+  int32_t kind;            /* kvs_kind                                          */
+  int32_t basis_rank;      /* factorized: R, basis rows per pair (32)          */
+  int32_t resid_rank_max;  /* factorized: Rmax, residual codes per token (16)  */
+  int32_t max_batch;       /* sequences the cache holds                        */
+  int32_t max_ctx;         /* tokens per sequence the cache holds               */
+} kvs_config;
+
+/* Immutable host-side plan built from a sharing map.  Thread-safe to share. */
+typedef struct kvs_plan kvs_plan;
+
+/* What one layer reads.  Owner slots are numbered 0.. in ascending order of
+ * the layers that own cache entries. */
+typedef struct {
+  int32_t owns_kv;         /* 1: the layer writes its own cache entries        */
+  int32_t n_src;           /* 1 or 2                                            */
+  int32_t src_layer[2];    /* source layers (-1 when unused)                    */
+  int32_t src_slot[2];     /* their owner slots (-1 when unused)                */
+  float   weight[2];       /* mixing weights as stored (fp32)                   */
+} kvs_layer_info;
+
+typedef struct {
+  int32_t n_layers;
+  int32_t n_slots;           /* owner slots = layers holding cache entries     */
+  int32_t last_owner_layer;  /* deepest owner; deeper layers write no cache     */
+  int32_t n_mixed_layers;    /* layers reading two sources                      */
+} kvs_plan_info;
+
+/* Byte sizes of the caller-allocated device buffers.  Pool layouts (64-token
+ * pages; page p of sequence b lives in physical page page_table[b][p]):
+ *   dense K pool  [n_slots][n_phys_pages][Hkv][hd/E][64][E]   E = 16 B / elem
+ *   dense V pool  [n_slots][n_phys_pages][Hkv][32][hd][2]     token pairs
+ *                 (element (t, d) of a page at (t/2)*hd*2 + d*2 + t%2)
+ *   page table    [max_batch][pages_per_seq] int32 in [0, n_phys_pages)
+ *   factorized:
+ *     cK / cV     [n_slots][n_phys_pages][Hkv][64][R]          bf16
+ *     dK / dV     [n_layers][n_phys_pages][Hkv][64][Rmax]      int8
+ *     sK / sV     [n_layers][n_phys_pages][Hkv][64]            fp16
+ *     rank        [n_phys_pages][64]                           uint8
+ *     BK / BV     [n_slots][Hkv][R][hd]                        bf16
+ *     UK / UV     [n_layers][Hkv][Rmax][hd]                    bf16       */
+typedef struct {
+  int32_t page_tokens;         /* 64                                           */
+  int32_t pages_per_seq;       /* ceil(max_ctx / 64)                           */
+  int32_t n_phys_pages;        /* max_batch * pages_per_seq                    */
+  int32_t n_slots;
+  size_t  k_pool_bytes;        /* dense: each of the K and V pools             */
+  size_t  v_pool_bytes;
+  size_t  page_table_bytes;
+  size_t  coef_pool_bytes;     /* factorized: each of cK, cV                   */
+  size_t  resid_pool_bytes;    /* factorized: each of dK, dV                   */
+  size_t  scale_pool_bytes;    /* factorized: each of sK, sV                   */
+  size_t  rank_pool_bytes;     /* factorized                                   */
+  size_t  basis_bytes;         /* factorized: each of BK, BV                   */
+  size_t  resid_basis_bytes;   /* factorized: each of UK, UV                   */
+} kvs_cache_sizes;
+
+/* Device pointers of one cache instance (all caller-owned). */
+typedef struct {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* page_table;
+  void* ck_pool;
+  void* cv_pool;
+  void* dk_pool;
+  void* dv_pool;
+  void* sk_pool;
+  void* sv_pool;
+  void* rank_pool;
+  const void* basis_k;
+  const void* basis_v;
+  const void* ubasis_k;
+  const void* ubasis_v;
+} kvs_cache;
+
+/* ---------------------------------------------------------------- planning */
+
+/* Build a plan from a sharing map.
+ *   src  [n_layers][2] host int32: source layers of each layer; the second
+ *        entry is -1 for a single source.  A layer owns its cache entries iff
+ *        its row is (l, -1) with weight 1.
+ *   w    [n_layers][2] host float or NULL (NULL: all weights 1).
+ * Rules (first violation wins, layers scanned in order): indices in range and
+ * weights finite, else KVS_ERR_MAP; a row naming its own layer must be the
+ * plain owner row, else KVS_ERR_MAP; a source above its reader ->
+ * KVS_ERR_UNSUPPORTED (top/middle configurations); a source that owns no
+ * entries -> KVS_ERR_NOT_SOURCE (reusing layers compute no K/V, CLA
+ * Methodology, so chains are invalid).  KVS_FACTORIZED plans take single
+ * sources only: src[l][0] is the layer that writes the pair's coefficients.
+ * On success *out receives a plan to release with kvs_plan_free(). */
+KVS_API kvs_status kvs_share_plan(const kvs_config* cfg, const int32_t* src,
+                                  const float* w, kvs_plan** out);
+KVS_API void kvs_plan_free(kvs_plan* plan);
+KVS_API kvs_status kvs_plan_layer(const kvs_plan* plan, int32_t layer,
+                                  kvs_layer_info* out);
+KVS_API kvs_status kvs_plan_summary(const kvs_plan* plan, kvs_plan_info* out);
+KVS_API kvs_status kvs_cache_layout(const kvs_plan* plan, kvs_cache_sizes* out);
+
+/* Split-K partitions per (sequence, KV head) the decode uses when n_splits=0
+ * is passed to kvs_attn_decode: chosen from batch, KV heads and the longest
+ * sequence so the launch fills the GPU; partition boundaries fall on 64-key
+ * page boundaries. */
+KVS_API kvs_status kvs_decode_splits(const kvs_plan* plan, int32_t batch,
+                                     int32_t max_seq_len, int32_t* n_splits);
+/* Workspace bytes kvs_attn_decode needs for (batch, n_splits). */
+KVS_API kvs_status kvs_decode_workspace_size(const kvs_plan* plan, int32_t batch,
+                                             int32_t n_splits, size_t* bytes);
+
+/* ----------------------------------------------------------------- writing */
+
+/* Write n new tokens' K/V of an owner layer into its slot.
+ *   k, v       device [batch][n][Hkv][hd], cache dtype
+ *   start_pos  device int32 [batch]: token i of sequence b goes to position
+ *              start_pos[b] + i.  Positions outside [0, max_ctx), or whose
+ *              page-table entry is outside [0, n_phys_pages), are skipped.
+ * Errors: layer not an owner -> KVS_ERR_NOT_SOURCE; n > max_ctx or
+ * batch > max_batch -> KVS_ERR_RANGE; factorized plan -> KVS_ERR_ARG. */
+KVS_API kvs_status kvs_append(const kvs_plan* plan, const kvs_cache* cache, int32_t layer,
+                              const void* k, const void* v, int32_t n,
+                              const int32_t* start_pos, int32_t batch, void* stream);
+
+/* Factorized write of n tokens for `layer`.
+ *   ck, cv     device bf16 [batch][n][Hkv][R]: the pair coefficients; given
+ *              only by the layer that owns the pair's slot (else NULL)
+ *   dk, dv     device int8 [batch][n][Hkv][Rmax]; codes at j >= r_t are
+ *              stored but never read
+ *   sk, sv     device fp16 [batch][n][Hkv]
+ *   rank       device uint8 [batch][n] in [0, Rmax], or NULL to leave the
+ *              stored ranks unchanged (ranks are per token, shared by layers)
+ *   start_pos  as for kvs_append. */
+KVS_API kvs_status kvs_append_factorized(const kvs_plan* plan, const kvs_cache* cache,
+                                         int32_t layer, const void* ck, const void* cv,
+                                         const int8_t* dk, const int8_t* dv,
+                                         const void* sk, const void* sv,
+                                         const uint8_t* rank, int32_t n,
+                                         const int32_t* start_pos, int32_t batch,
+                                         void* stream);
+
+/* ---------------------------------------------------------------- attention */
+
+/* One decode query per (sequence, q head) of `layer` over keys
+ * 0..seq_len[b]-1 of the layer's source(s) (the current token's entry
+ * included: its owner appends it first).
+ *   q           device [batch][Hq][hd], cache dtype (bf16 for factorized)
+ *   seq_len     device int32 [batch]; values are clamped to [0, max_ctx]; a
+ *               sequence with no keys yields zeros
+ *   max_seq_len host: the largest seq_len (used only to pick n_splits)
+ *   n_splits    split-K partitions per (sequence, KV head); 0 = library choice
+ *   out         device [batch][Hq][hd] of out_dtype (KVS_F32 or KVS_BF16)
+ *   workspace   device, >= kvs_decode_workspace_size(batch, n_splits) bytes
+ * Result is deterministic for fixed n_splits. */
+KVS_API kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cache,
+                                   int32_t layer, const void* q, const int32_t* seq_len,
+                                   int32_t batch, int32_t max_seq_len, int32_t n_splits,
+                                   void* out, int32_t out_dtype, void* workspace,
+                                   size_t ws_bytes, void* stream);
+
+/* A chunk of n queries per sequence that sit at the last n positions of each
+ * sequence (their K/V already appended): query i of sequence b is at
+ * P = seq_len[b] - n + i and sees keys 0..P when causal != 0 (inclusive
+ * diagonal), else keys 0..seq_len[b]-1.  Query and key tiles go through bf16
+ * MFMA with fp32 accumulation; a two-source layer's mixed K~/V~ tiles are
+ * rounded to bf16 before the MFMA.
+ *   q        device bf16 [batch][n][Hq][hd]
+ *   seq_len  device int32 [batch], each >= n
+ *   out      device [batch][n][Hq][hd] of out_dtype
+ * Dense bf16 plans only (KVS_ERR_UNSUPPORTED otherwise). */
+KVS_API kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cache* cache,
+                                          int32_t layer, const void* q, int32_t n,
+                                          const int32_t* seq_len, int32_t batch,
+                                          int32_t causal, void* out, int32_t out_dtype,
+                                          void* stream);
+
+/* Description of the last error on this thread ("" if none). */
+KVS_API const char* kvs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVSHARE_H */

@@ -241,7 +241,7 @@ def test_brute_force_factorized_tiny():
 def _small_dense(share, L, seed_shift=0):
     wl = datagen.WORKLOADS["depthgraft" if share == "depthgraft" else "tinyllama_cla2"]
     wl = wl.with_(n_layers=L, batch=2, ctx=40, n_q_heads=8, n_kv_heads=2, head_dim=16,
-                  seed=wl.seed + seed_shift)
+                  seed=wl.seed + seed_shift, dg_stride=2)
     src, w = datagen.share_map(wl)
     ok = datagen.owner_layers(src)
     kk, vv = {}, {}
