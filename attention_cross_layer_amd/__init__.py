@@ -294,7 +294,8 @@ def kvs_attn_decode(plan: Plan, cache: Cache, layer: int, q: torch.Tensor,
     if n_splits == 0:
         n_splits = kvs_decode_splits(plan, B, max_seq_len)
     if workspace is None:
-        workspace = torch.empty(kvs_decode_workspace_size(plan, B, n_splits), dtype=torch.uint8,
+        # zero-filled: the library's per-(sequence, KV head) counters start at zero
+        workspace = torch.zeros(kvs_decode_workspace_size(plan, B, n_splits), dtype=torch.uint8,
                                 device=q.device)
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)

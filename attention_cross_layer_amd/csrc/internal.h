@@ -31,6 +31,8 @@ inline size_t elem_bytes(int32_t dtype) { return dtype == KVS_F32 ? 4 : 2; }
 
 // Whether the decode kernels are instantiated for this shape and source count.
 bool decode_shape_supported(int32_t dtype, int32_t head_dim, int32_t group, int32_t n_src);
+// Largest split-K partition count one decode launch merges.
+int max_decode_splits();
 
 // ------------------------------------------------------------ HIP launchers
 // Implemented in the .hip files; each returns a hipError_t value (0 = ok).

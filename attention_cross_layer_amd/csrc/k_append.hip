@@ -4,9 +4,12 @@
 // new K/V, the others reuse it), so the pools hold source layers only.
 //
 // Page layouts (64 tokens per page, per KV head):
-//   K  [hd/E][64][E]   E = 16 bytes of elements: chunk c of token t at
-//                      c*64*E + t*E -- a key row is hd/E 16-byte chunks
-//   V  [32][hd][2]     token pairs: element (t, d) at (t/2)*hd*2 + d*2 + t%2
+//   K  [4][NCQ][16][4][E]  E = elements per 16 bytes, NCQ = hd/(4E): chunk
+//                          c = 4*cc + qd of token t = 16*j + k16 sits at
+//                          ((j*NCQ + cc)*64 + 4*k16 + qd)*E, so the decode's
+//                          lane 4*k16 + qd loads one contiguous 1 KiB per
+//                          (j, cc) and holds a quarter of 16 keys' rows
+//   V  [32][hd][2]         token pairs: element (t, d) at (t/2)*hd*2 + d*2 + t%2
 // One thread moves one 16-byte chunk of the input row; byte copy, no
 // arithmetic on the values.
 #include <hip/hip_runtime.h>
@@ -39,8 +42,10 @@ __global__ __launch_bounds__(256) void append_kernel(AppendLaunch a) {
   const size_t tile = ((size_t)page * a.n_kv_heads + kvh) * kPage * hd + a.slot_offset;
   const size_t src = (((size_t)b * a.n + i) * a.n_kv_heads + kvh) * hd + (size_t)c * E;
 
+  const int ncq = nch / 4;
+  const size_t kdst = ((size_t)((t >> 4) * ncq + (c >> 2)) * kPage + (t & 15) * 4 + (c & 3)) * E;
   const uint4 kv = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k) + src);
-  *reinterpret_cast<uint4*>(static_cast<T*>(a.k_pool) + tile + (size_t)c * kPage * E + t * E) = kv;
+  *reinterpret_cast<uint4*>(static_cast<T*>(a.k_pool) + tile + kdst) = kv;
 
   const T* vs = static_cast<const T*>(a.v) + src;
   T* vd = static_cast<T*>(a.v_pool) + tile + (size_t)(t >> 1) * hd * 2 + (t & 1);

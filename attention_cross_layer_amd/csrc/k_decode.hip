@@ -1,5 +1,5 @@
-// Split-K decode attention over a shared (paged, source-only) K/V cache, and
-// the combine of the per-partition partial results.
+// Split-K decode attention over a shared (paged, source-only) K/V cache, with
+// the merge of the split-K partitions fused into the same launch.
 //
 // One decode query per (sequence, q head) attends over keys 0..seq_len-1 of
 // the layer's source slot(s): the CLA page ("Reducing Transformer Key-Value
@@ -12,26 +12,37 @@
 // forming K~/V~: every product stays an exact bf16 x bf16 product.
 //
 // Work decomposition (gfx950, wave64):
-//   grid (ceil(n_splits / 4), Hkv, B), 256 threads = 4 independent waves.
-//   Each wave owns one split-K partition: a run of whole 64-key pages of one
-//   (sequence, KV head).  All G query heads of that KV head are served by
-//   the same pass, so every cached tile is read from HBM once per
-//   (sequence, KV head) -- once for the whole query group.
-//   Per page:
-//     QK   lane t owns key t.  The K page is stored as [hd/E][64][E] (E
-//          elements = 16 bytes), so chunk c of all 64 keys is one contiguous
-//          1 KiB load.  The G query rows are broadcast from LDS; scores use
-//          v_dot2c_f32_bf16 (fp32 accumulate).
-//     softmax  wave-wide max per head over DPP, running max/sum rescaling
-//          (online softmax); probabilities are rounded to bf16 for the PV
-//          products and the running sum uses the same rounded values.
-//     PV   the V page is stored as token pairs [32][hd][2], so a 16-byte load
-//          holds 4 dims x 2 keys; lane l owns dims 4*(l % (hd/4)) and every
-//          NPH-th pair; each dword feeds v_dot2c_f32_bf16 with the pair's two
-//          probabilities read from LDS.
-//   A partition's result (unnormalised O, running max m, running sum l; log2
-//   domain) goes to the workspace; the combine kernel merges partitions in
-//   fixed order, so results are deterministic for a fixed split count.
+//   grid (S, Hkv, B), 256 threads = 4 waves.  Workgroup s owns split-K
+//   partition s of one (sequence, KV head): an even share of its 64-key
+//   pages; wave w takes every 4th page of it.  All G query heads of the KV
+//   head are served by the same pass, so each cached tile is read from HBM
+//   once per (sequence, KV head), i.e. once for the whole query group.
+//   Per page, per wave:
+//     QK   four lanes share a key: lane 4*k16 + qd holds, in registers for
+//          the whole launch, the query chunks 4*cc + qd (E elements = 16
+//          bytes each) of all G heads.  Pass j (0..3) scores keys 16j + k16:
+//          the K page layout puts each (j, cc) slice of 64 lanes x 16 bytes
+//          in one contiguous 1 KiB load; partial dot products
+//          (v_dot2c_f32_bf16: bf16 x bf16 products, fp32 accumulation) are
+//          completed by two quad_perm DPP adds.  Lane qd then keeps the
+//          scores of pass qd, i.e. key 16*qd + k16.
+//     softmax  per-head wave max over DPP, online rescaling; probabilities
+//          are rounded to bf16 for the PV products and the running sum uses
+//          the same rounded values.
+//     PV   the V page is stored as token pairs [32][hd][2], so one 16-byte
+//          load holds 4 dims x 2 keys; lane l owns 4 dims and every NPH-th
+//          pair, each dword feeding v_dot2c_f32_bf16 with the pair's two
+//          probabilities (read from LDS).
+//   The next page's K is requested as soon as the scores are done and its V
+//   as soon as the PV products are done, so loads overlap the other half of
+//   the page's work.
+//   Merge: the 4 waves' (O, m, l) meet in LDS.  With S = 1 the workgroup
+//   writes the normalised output.  Otherwise it writes its partition to the
+//   workspace and a small merge kernel on the same stream combines the S
+//   partitions in fixed order, so results are deterministic for a fixed S.
+//   (Merging inside the decode launch would need an agent-scope release per
+//   workgroup, i.e. an L2 write-back per workgroup; that measured several
+//   times slower than the second launch.)
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -43,6 +54,8 @@ namespace kvs {
 namespace {
 
 using dev::dot2_bf16;
+
+constexpr int kMaxFusedSplits = 64;
 
 struct DecodeParams {
   const char* k_pool;
@@ -63,6 +76,8 @@ struct DecodeParams {
   float* ws_o;           // [B][Hq][S][HD]
   float* ws_m;           // [B][Hq][S]
   float* ws_l;           // [B][Hq][S]
+  void* out;             // [B][Hq][HD]
+  int out_bf16;
 };
 
 // Storage traits.  bf16 elements are carried as raw 16-bit patterns.
@@ -115,21 +130,18 @@ __device__ __forceinline__ void pair_fma(float* acc, float2 pp, const uint4& v, 
 }
 
 // Zero the entries of keys >= nvalid in a V pair load (pool memory past the
-// sequence end is unwritten and may hold NaN patterns; p = 0 there, but
-// 0 * NaN is NaN).
+// sequence end may hold NaN patterns; p = 0 there, but 0 * NaN is NaN).
+// Branch-free: the key index differs per lane.
 __device__ __forceinline__ void mask_pair(uint4& v, int key0, int nvalid, uint16_t) {
-  if (key0 >= nvalid) {
-    v = make_uint4(0, 0, 0, 0);
-  } else if (key0 + 1 >= nvalid) {
-    v.x &= 0xffffu; v.y &= 0xffffu; v.z &= 0xffffu; v.w &= 0xffffu;
-  }
+  const uint32_t lo = key0 < nvalid ? 0x0000ffffu : 0u;
+  const uint32_t hi = key0 + 1 < nvalid ? 0xffff0000u : 0u;
+  const uint32_t mk = lo | hi;
+  v.x &= mk; v.y &= mk; v.z &= mk; v.w &= mk;
 }
 __device__ __forceinline__ void mask_pair(uint4& v, int key0, int nvalid, float) {
-  if (key0 >= nvalid) {
-    v = make_uint4(0, 0, 0, 0);
-  } else if (key0 + 1 >= nvalid) {
-    v.y = 0; v.w = 0;
-  }
+  const uint32_t m0 = key0 < nvalid ? 0xffffffffu : 0u;
+  const uint32_t m1 = key0 + 1 < nvalid ? 0xffffffffu : 0u;
+  v.x &= m0; v.y &= m1; v.z &= m0; v.w &= m1;
 }
 
 __device__ __forceinline__ void store_prob(uint32_t* pl, int idx, int half, float p, float& used) {
@@ -142,8 +154,36 @@ __device__ __forceinline__ void store_prob(float2* pl, int idx, int half, float 
   reinterpret_cast<float*>(pl)[idx * 2 + half] = p;
 }
 
+__device__ __forceinline__ void store_out(void* out, size_t idx, float v, int bf16) {
+  if (bf16)
+    reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)dev::f32_to_bf16_bits(v);
+  else
+    reinterpret_cast<float*>(out)[idx] = v;
+}
+
+template <typename T, int HD, int NSRC>
+__device__ __forceinline__ void load_k(uint4 (&kr)[NSRC][HD / Traits<T>::E], const T* const (&kt)[NSRC],
+                                       int lane) {
+  constexpr int E = Traits<T>::E;
+#pragma unroll
+  for (int s = 0; s < NSRC; ++s)
+#pragma unroll
+    for (int c = 0; c < HD / E; ++c)
+      kr[s][c] = *reinterpret_cast<const uint4*>(kt[s] + c * (kPage * E) + lane * E);
+}
+
+template <typename T, int HD, int NSRC, int PPL, int NPH, int DPL>
+__device__ __forceinline__ void load_v(uint4 (&vr)[NSRC][PPL], const T* const (&vt)[NSRC], int ph,
+                                       int quad) {
+#pragma unroll
+  for (int s = 0; s < NSRC; ++s)
+#pragma unroll
+    for (int j = 0; j < PPL; ++j)
+      vr[s][j] = *reinterpret_cast<const uint4*>(vt[s] + (ph + NPH * j) * (HD * 2) + quad * (DPL * 2));
+}
+
 template <typename T, int HD, int G, int NSRC>
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams a) {
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
   typedef Traits<T> Tr;
   typedef typename Tr::Pair Pair;
   constexpr int E = Tr::E;
@@ -153,28 +193,43 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams a) {
   constexpr int NPH = 64 / NQ;       // pair phases
   constexpr int PPL = 32 / NPH;      // pairs per lane per page
 
-  __shared__ uint4 q_lds[G * NCH];
+  constexpr int NCQ = NCH / 4;       // chunks of a key row per lane (a quarter)
+
   __shared__ Pair p_lds[4][32 * G];
+  __shared__ float mrg_o[4][G][HD];
+  __shared__ float mrg_m[4][G];
+  __shared__ float mrg_l[4][G];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // wave index as a scalar, so page loop control stays in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int split = blockIdx.x;
   const int kvh = blockIdx.y;
-  const int split = blockIdx.x * 4 + wave;
+  const int b = blockIdx.z;
+  const int S = a.n_splits;
 
+  // QK lane roles: 4 lanes share a key; lane (k16, qd) = 4*k16 + qd holds the
+  // query chunks 4*cc + qd of every head in registers for the whole launch.
+  const int qd = lane & 3;
+  const int k16 = lane >> 2;
+  uint4 qreg[G][NCQ];
   {
     const uint4* qsrc = reinterpret_cast<const uint4*>(
         a.q + ((size_t)b * a.n_q_heads + (size_t)kvh * G) * HD * sizeof(T));
-    for (int i = threadIdx.x; i < G * NCH; i += 256) q_lds[i] = qsrc[i];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int cc = 0; cc < NCQ; ++cc) qreg[h][cc] = qsrc[h * NCH + 4 * cc + qd];
   }
-  __syncthreads();
-  if (split >= a.n_splits) return;
+  // after the quad reduction each lane keeps the scores of one key of the
+  // page: pass qd, i.e. key 16*qd + k16
+  const int my_key = 16 * qd + k16;
 
   const int n_keys = clamp_len(a.seq_len[b], a.max_ctx);
   const int n_pages = (n_keys + kPage - 1) / kPage;
   int pb, pe;
-  split_range(n_pages, split, a.n_splits, pb, pe);
-  if (pb >= pe) return;
+  split_range(n_pages, split, S, pb, pe);
 
   const int quad = lane % NQ;
   const int ph = lane / NQ;
@@ -194,44 +249,62 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams a) {
 
   const int64_t slot_off[2] = {(int64_t)a.slot0 * a.slot_stride, (int64_t)a.slot1 * a.slot_stride};
   const int32_t* pt = a.page_table + (size_t)b * a.pages_per_seq;
+  const T* kbase = reinterpret_cast<const T*>(a.k_pool);
+  const T* vbase = reinterpret_cast<const T*>(a.v_pool);
 
-  for (int pg = pb; pg < pe; ++pg) {
-    const int phys = pt[pg];
-    if ((unsigned)phys >= (unsigned)a.n_phys_pages) continue;   // corrupt entry: never read
-    const int64_t tile = ((int64_t)phys * a.n_kv_heads + kvh) * (kPage * HD);
+  // next page of this wave whose page-table entry is valid (corrupt entries
+  // are skipped, never read)
+  auto next_page = [&](int from) {
+    int p = from;
+    while (p < pe && (unsigned)pt[p] >= (unsigned)a.n_phys_pages) p += 4;
+    return p;
+  };
+  auto tiles = [&](int p, const T* (&kt)[NSRC], const T* (&vt)[NSRC]) {
+    const int64_t tile = ((int64_t)pt[p] * a.n_kv_heads + kvh) * (kPage * HD);
+#pragma unroll
+    for (int s = 0; s < NSRC; ++s) {
+      kt[s] = kbase + slot_off[s] + tile;
+      vt[s] = vbase + slot_off[s] + tile;
+    }
+  };
+
+  for (int pg = next_page(pb + wave); pg < pe; pg = next_page(pg + 4)) {
+    // both halves of the page are requested up front; the scores wait only
+    // for K, while V is still in flight
     uint4 kr[NSRC][NCH];
     uint4 vr[NSRC][PPL];
-#pragma unroll
-    for (int s = 0; s < NSRC; ++s) {
-      const T* kt = reinterpret_cast<const T*>(a.k_pool) + slot_off[s] + tile;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c)
-        kr[s][c] = *reinterpret_cast<const uint4*>(kt + c * (kPage * E) + lane * E);
-    }
-#pragma unroll
-    for (int s = 0; s < NSRC; ++s) {
-      const T* vt = reinterpret_cast<const T*>(a.v_pool) + slot_off[s] + tile;
-#pragma unroll
-      for (int j = 0; j < PPL; ++j)
-        vr[s][j] = *reinterpret_cast<const uint4*>(vt + (ph + NPH * j) * (HD * 2) + quad * (DPL * 2));
+    {
+      const T* kt[NSRC];
+      const T* vt[NSRC];
+      tiles(pg, kt, vt);
+      load_k<T, HD, NSRC>(kr, kt, lane);
+      load_v<T, HD, NSRC, PPL, NPH, DPL>(vr, vt, ph, quad);
     }
 
-    // ---- scores, lane = key
+    // ---- scores: pass j covers keys 16j..16j+15, one quarter of the head
+    // dim per lane; the quad_perm DPP adds complete the dot products
     const int nvalid = n_keys - pg * kPage;   // >= 1
-    const bool key_ok = lane < nvalid;
     float sc[G];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float d0 = 0.f, d1 = 0.f;
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const uint4 qc = q_lds[h * NCH + c];
-        d0 = chunk_dot(qc, kr[0][c], d0, T());
-        if (NSRC == 2) d1 = chunk_dot(qc, kr[NSRC - 1][c], d1, T());
+      for (int h = 0; h < G; ++h) {
+        float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < NCQ; ++cc) {
+          d0 = chunk_dot(qreg[h][cc], kr[0][j * NCQ + cc], d0, T());
+          if (NSRC == 2) d1 = chunk_dot(qreg[h][cc], kr[NSRC - 1][j * NCQ + cc], d1, T());
+        }
+        float s = (NSRC == 2) ? fmaf(a.w0, d0, a.w1 * d1) : d0;
+        s += dev::dpp<0xB1>(s);   // quad_perm [1,0,3,2]
+        s += dev::dpp<0x4E>(s);   // quad_perm [2,3,0,1]
+        if (j == 0) sc[h] = s;
+        else sc[h] = (qd == j) ? s : sc[h];
       }
-      const float s = (NSRC == 2) ? fmaf(a.w0, d0, a.w1 * d1) : d0;
-      sc[h] = key_ok ? s * a.scale_log2 : -INFINITY;
     }
+    const bool key_ok = my_key < nvalid;
+#pragma unroll
+    for (int h = 0; h < G; ++h) sc[h] = key_ok ? sc[h] * a.scale_log2 : -INFINITY;
 
     // ---- online softmax
 #pragma unroll
@@ -241,7 +314,7 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams a) {
       const float alpha = dev::fast_exp2(m[h] - mn);
       m[h] = mn;
       float used;
-      store_prob(pl, (lane >> 1) * G + h, lane & 1, dev::fast_exp2(sc[h] - mn), used);
+      store_prob(pl, (my_key >> 1) * G + h, my_key & 1, dev::fast_exp2(sc[h] - mn), used);
       lsum[h] = fmaf(lsum[h], alpha, used);
 #pragma unroll
       for (int s = 0; s < NSRC; ++s)
@@ -270,12 +343,10 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams a) {
     __builtin_amdgcn_wave_barrier();
   }
 
-  // ---- write the partition's partial result
-  const int S = a.n_splits;
+  // ---- this wave's (O, m, l) to LDS
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float l = dev::wave_sum(lsum[h]);
-    float o[DPL];
 #pragma unroll
     for (int d = 0; d < DPL; ++d) {
       float x0 = acc[0][h][d];
@@ -287,79 +358,106 @@ __global__ __launch_bounds__(256) void decode_partial_kernel(DecodeParams a) {
         for (int off = NQ; off < 64; off <<= 1) x1 += __shfl_xor(x1, off);
         x0 = fmaf(a.w0, x0, a.w1 * x1);
       }
-      o[d] = x0;
-    }
-    const size_t row = ((size_t)b * a.n_q_heads + (size_t)kvh * G + h) * S + split;
-    if (lane < NQ) {
-      float* dst = a.ws_o + row * HD + quad * DPL;
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) dst[d] = o[d];
+      if (lane < NQ) mrg_o[wave][h][quad * DPL + d] = x0;
     }
     if (lane == 0) {
-      a.ws_m[row] = m[h];
-      a.ws_l[row] = l;
+      mrg_m[wave][h] = m[h];
+      mrg_l[wave][h] = l;
+    }
+  }
+  __syncthreads();
+
+  // ---- merge the 4 waves; write the output (S == 1) or the partition
+  const size_t hq0 = (size_t)b * a.n_q_heads + (size_t)kvh * G;
+  for (int e = tid; e < G * HD; e += 256) {
+    const int h = e / HD, d = e % HD;
+    float M = mrg_m[0][h];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, mrg_m[w][h]);
+    float o = 0.f, l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = dev::fast_exp2(mrg_m[w][h] - M);
+        o = fmaf(f, mrg_o[w][h][d], o);
+        l = fmaf(f, mrg_l[w][h], l);
+      }
+    }
+    if (S == 1) {
+      store_out(a.out, (hq0 + h) * HD + d, l > 0.f ? o / l : 0.f, a.out_bf16);
+    } else {
+      const size_t row = (hq0 + h) * S + split;
+      a.ws_o[row * HD + d] = o;
+      if (d == 0) {
+        a.ws_m[row] = M;
+        a.ws_l[row] = l;
+      }
     }
   }
 }
 
-// Merge the partitions of one (sequence, q head): out = sum_s 2^(m_s - M) O_s /
-// sum_s 2^(m_s - M) l_s, M = max_s m_s, in split order.  grid (Hq, B), 64 threads.
-template <int HD>
-__global__ __launch_bounds__(64) void decode_combine_kernel(const float* ws_o, const float* ws_m,
-                                                            const float* ws_l,
-                                                            const int32_t* seq_len, int max_ctx,
-                                                            int n_q_heads, int S, void* out,
-                                                            int out_bf16) {
-  constexpr int DPT = HD / 64;
-  const int hq = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
-  const int n_keys = clamp_len(seq_len[b], max_ctx);
+// Merge of the S partitions of one (sequence, KV head): for each of its G
+// query heads, out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with
+// M = max_s m_s, summed in partition order (deterministic).  Partitions with
+// no pages were never written and are skipped.  grid (Hkv, B), 256 threads;
+// all loads of a thread are independent, so they overlap.
+template <int G, int HD>
+__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams a) {
+  __shared__ float f_lds[G * kMaxFusedSplits];
+  __shared__ float den_lds[G];
+  const int tid = threadIdx.x;
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int S = a.n_splits;
+  const int n_keys = clamp_len(a.seq_len[b], a.max_ctx);
   const int n_pages = (n_keys + kPage - 1) / kPage;
-  const size_t row0 = ((size_t)b * n_q_heads + hq) * S;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) {
-    int pb, pe;
-    split_range(n_pages, s, S, pb, pe);
-    if (pb < pe) M = fmaxf(M, ws_m[row0 + s]);
+  const size_t hq0 = (size_t)b * a.n_q_heads + (size_t)kvh * G;
+  for (int i = tid; i < G * S; i += 256) {
+    const int h = i / S, s = i % S;
+    int qb, qe;
+    split_range(n_pages, s, S, qb, qe);
+    f_lds[i] = qb < qe ? a.ws_m[(hq0 + h) * S + s] : -INFINITY;
   }
-  float den = 0.f, num[DPT];
-#pragma unroll
-  for (int d = 0; d < DPT; ++d) num[d] = 0.f;
-  for (int s = 0; s < S; ++s) {
-    int pb, pe;
-    split_range(n_pages, s, S, pb, pe);
-    if (pb >= pe) continue;
-    const float f = dev::fast_exp2(ws_m[row0 + s] - M);
-    den = fmaf(f, ws_l[row0 + s], den);
-    const float* o = ws_o + (row0 + s) * HD;
-#pragma unroll
-    for (int d = 0; d < DPT; ++d) num[d] = fmaf(f, o[lane + 64 * d], num[d]);
+  __syncthreads();
+  if (tid < G) {
+    const int h = tid;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, f_lds[h * S + s]);
+    float den = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float ms = f_lds[h * S + s];
+      const float f = (ms == -INFINITY) ? 0.f : dev::fast_exp2(ms - M);
+      if (f != 0.f) den = fmaf(f, a.ws_l[(hq0 + h) * S + s], den);
+      f_lds[h * S + s] = f;
+    }
+    den_lds[h] = den;
   }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  const size_t orow = ((size_t)b * n_q_heads + hq) * HD;
-#pragma unroll
-  for (int d = 0; d < DPT; ++d) {
-    const float r = num[d] * inv;
-    if (out_bf16)
-      reinterpret_cast<uint16_t*>(out)[orow + lane + 64 * d] = (uint16_t)dev::f32_to_bf16_bits(r);
-    else
-      reinterpret_cast<float*>(out)[orow + lane + 64 * d] = r;
+  __syncthreads();
+  for (int e = tid; e < G * HD; e += 256) {
+    const int h = e / HD, d = e % HD;
+    const float* o = a.ws_o + (hq0 + h) * S * HD + d;
+    float num = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) {
+      const float f = f_lds[h * S + s];
+      const float x = o[(size_t)s * HD];
+      num = (f != 0.f) ? fmaf(f, x, num) : num;   // unwritten partitions hold stale bytes
+    }
+    const float den = den_lds[h];
+    store_out(a.out, (hq0 + h) * HD + d, den > 0.f ? num / den : 0.f, a.out_bf16);
   }
 }
 
 template <typename T, int HD, int G, int NSRC>
-int run_decode(const DecodeParams& p, int B, int S, int Hkv, const int32_t* seq_len, int max_ctx,
-               void* out, int out_bf16, hipStream_t st) {
-  dim3 grid((S + 3) / 4, Hkv, B);
-  hipLaunchKernelGGL((decode_partial_kernel<T, HD, G, NSRC>), grid, dim3(256), 0, st, p);
+int run_decode(const DecodeParams& p, int B, hipStream_t st) {
+  dim3 grid(p.n_splits, p.n_kv_heads, B);
+  hipLaunchKernelGGL((decode_kernel<T, HD, G, NSRC>), grid, dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return (int)e;
-  hipLaunchKernelGGL((decode_combine_kernel<HD>), dim3(p.n_q_heads, B), dim3(64), 0, st, p.ws_o,
-                     p.ws_m, p.ws_l, seq_len, max_ctx, p.n_q_heads, S, out, out_bf16);
+  if (e != hipSuccess || p.n_splits == 1) return (int)e;
+  hipLaunchKernelGGL((decode_merge_kernel<G, HD>), dim3(p.n_kv_heads, B), dim3(256), 0, st, p);
   return (int)hipGetLastError();
 }
 
-typedef int (*DecodeFn)(const DecodeParams&, int, int, int, const int32_t*, int, void*, int,
-                        hipStream_t);
+typedef int (*DecodeFn)(const DecodeParams&, int, hipStream_t);
 
 template <typename T, int HD, int NSRC>
 DecodeFn pick_group(int G) {
@@ -393,13 +491,15 @@ DecodeFn pick(int dtype, int hd, int G, int nsrc) {
 
 }  // namespace
 
+int max_decode_splits() { return kMaxFusedSplits; }
+
 bool decode_shape_supported(int32_t dtype, int32_t head_dim, int32_t group, int32_t n_src) {
   return pick(dtype, head_dim, group, n_src) != nullptr;
 }
 
 int launch_decode(const DecodeLaunch& a, void* stream) {
   DecodeFn fn = pick(a.dtype, a.head_dim, a.group, a.n_src);
-  if (!fn) return (int)hipErrorInvalidValue;
+  if (!fn || a.n_splits < 1 || a.n_splits > kMaxFusedSplits) return (int)hipErrorInvalidValue;
   DecodeParams p;
   p.k_pool = static_cast<const char*>(a.k_pool);
   p.v_pool = static_cast<const char*>(a.v_pool);
@@ -422,8 +522,9 @@ int launch_decode(const DecodeLaunch& a, void* stream) {
   p.ws_o = a.ws;
   p.ws_m = a.ws + rows * a.head_dim;
   p.ws_l = p.ws_m + rows;
-  return fn(p, a.batch, a.n_splits, a.n_kv_heads, a.seq_len, a.max_ctx, a.out,
-            a.out_dtype == KVS_BF16, static_cast<hipStream_t>(stream));
+  p.out = a.out;
+  p.out_bf16 = a.out_dtype == KVS_BF16;
+  return fn(p, a.batch, static_cast<hipStream_t>(stream));
 }
 
 const char* hip_error_name(int err) { return hipGetErrorString((hipError_t)err); }

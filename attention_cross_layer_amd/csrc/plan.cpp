@@ -165,11 +165,12 @@ extern "C" kvs_status kvs_cache_layout(const kvs_plan* plan, kvs_cache_sizes* ou
   return KVS_OK;
 }
 
-// Split-K choice: enough partitions that batch * n_kv_heads * n_splits waves
-// cover the GPU (256 CUs, several waves each), but at least two pages per
-// partition so each wave streams a few tiles after loading its queries.
-static const int32_t kTargetWaves = 4096;
-static const int32_t kMaxSplits = 1024;
+// Split-K choice.  A decode launch has one 4-wave workgroup per (partition,
+// KV head, sequence).  Aim for kTargetGroups workgroups (two per CU on the
+// 256-CU MI355X) while keeping at least 4 pages (one per wave) per
+// partition; at most max_decode_splits() partitions (the fused merge keeps
+// one weight per partition in LDS).
+static const int32_t kTargetGroups = 512;
 
 extern "C" kvs_status kvs_decode_splits(const kvs_plan* plan, int32_t batch, int32_t max_seq_len,
                                         int32_t* n_splits) {
@@ -179,24 +180,25 @@ extern "C" kvs_status kvs_decode_splits(const kvs_plan* plan, int32_t batch, int
   int32_t seq = max_seq_len < 1 ? 1 : (max_seq_len > plan->p.cfg.max_ctx ? plan->p.cfg.max_ctx : max_seq_len);
   const int32_t pages = (seq + kPage - 1) / kPage;
   const int32_t groups = batch * plan->p.cfg.n_kv_heads;
-  int32_t s = (kTargetWaves + groups - 1) / groups;
-  const int32_t cap = pages >= 4 ? pages / 2 : 1;
+  int32_t s = (kTargetGroups + groups - 1) / groups;
+  const int32_t cap = pages / 4;
   if (s > cap) s = cap;
-  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > max_decode_splits()) s = max_decode_splits();
   if (s < 1) s = 1;
   *n_splits = s;
   return KVS_OK;
 }
 
+// Workspace: per-partition partial results [B][Hq][S][hd] fp32, then the
+// running maxima and sums [B][Hq][S] fp32 each.
 extern "C" kvs_status kvs_decode_workspace_size(const kvs_plan* plan, int32_t batch,
                                                 int32_t n_splits, size_t* bytes) {
   clear_error();
   if (!plan || !bytes) return fail(KVS_ERR_ARG, "null argument");
   if (batch < 1 || batch > plan->p.cfg.max_batch) return fail(KVS_ERR_RANGE, "batch out of range");
-  if (n_splits < 1 || n_splits > kMaxSplits) return fail(KVS_ERR_RANGE, "n_splits out of range");
+  if (n_splits < 1 || n_splits > max_decode_splits()) return fail(KVS_ERR_RANGE, "n_splits out of range");
   const kvs_config& c = plan->p.cfg;
-  const int32_t width = c.kind == KVS_DENSE ? c.head_dim : c.head_dim;
-  *bytes = size_t(batch) * c.n_q_heads * n_splits * (width + 2) * sizeof(float);
+  *bytes = size_t(batch) * c.n_q_heads * n_splits * (c.head_dim + 2) * sizeof(float);
   return KVS_OK;
 }
 

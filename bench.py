@@ -3,21 +3,25 @@
 A step is one decode step of the whole hot path over all layers of the
 workload: every owner layer appends its new token's K/V (kvs_append, n=1),
 then every layer runs split-K decode attention over its source slot(s)
-(kvs_attn_decode: partial + combine).  Inputs are resident in HBM before the
-timed region; K/V and queries are seeded synthetic N(0,1) tensors of the
-workload's shapes.
+(kvs_attn_decode, one launch: partitions + fused merge).  Inputs are
+resident in HBM before the timed region; K/V and queries are seeded
+synthetic N(0,1) tensors of the workload's shapes.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--roofline-only] [--no-cpu-baseline]
 
 Prints one JSON line.  ``value`` is decode tokens/s (one token per sequence
-per step).  ``roofline`` rates the decode kernel launch (partial + combine)
-against the 8 TB/s HBM peak with the algorithmic bytes: every source tile read
-once per layer call.  ``cpu_baseline`` times the fp64 oracle on a bounded
-sample of sequences on the host.
+per step, warm back-to-back steps).  ``roofline`` rates the decode launch of
+a single-source layer against the 8 TB/s HBM peak with its algorithmic bytes
+(every source tile, K and V, read once): its duration is timed with HIP
+events on the launch stream with the 256 MB Infinity Cache flushed before
+each launch by reading a 512 MB buffer (a read leaves no dirty lines whose
+write-back would compete with the timed launch), so no byte of the timed
+launch is served from a cache.
+``cpu_baseline`` times the fp64 oracle on a bounded sample of sequences.
 """
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -32,25 +36,28 @@ import datagen  # noqa: E402
 
 METRIC = "shared-KV decode attn: tokens/s and achieved HBM GB/s (% of peak) per batch x ctx"
 HBM_PEAK_GBS = 8000.0
+FLUSH_BYTES = 512 << 20
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def describe(wl):
-    src, w = datagen.share_map(wl)
+def describe(wl, src):
     owners = datagen.owner_layers(src)
+    mixed = sum(1 for l in range(wl.n_layers) if int(src[l, 1]) >= 0)
     return {"workload": wl.name, "layers": wl.n_layers, "owner_layers": len(owners),
-            "batch": wl.batch, "ctx": wl.ctx, "q_heads": wl.n_q_heads,
+            "mixed_layers": mixed, "batch": wl.batch, "ctx": wl.ctx, "q_heads": wl.n_q_heads,
             "kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim, "share": wl.share,
             "peaky_frac": wl.peaky_frac}
 
 
-def algorithmic_bytes(wl, src):
-    """Bytes a layer call must read: each source tile (K and V) once."""
-    per_source = wl.batch * wl.n_kv_heads * wl.ctx * wl.head_dim * 2 * (4 if wl.dtype == "f32" else 2)
-    return [per_source * (1 if int(src[l, 1]) < 0 else 2) for l in range(wl.n_layers)]
+def bytes_per_call(wl, src, l):
+    """Algorithmic bytes of one decode call of layer l: every source tile (K and
+    V) read once; queries and outputs (< 0.5%) not counted."""
+    elem = 4 if wl.dtype == "f32" else 2
+    per_source = wl.batch * wl.n_kv_heads * wl.ctx * wl.head_dim * 2 * elem
+    return per_source * (1 if int(src[l, 1]) < 0 else 2)
 
 
 def setup(wl):
@@ -69,29 +76,27 @@ def setup(wl):
     return src, w, plan, cache, owners
 
 
-def cpu_baseline(wl, src, w, cache_host_fn, budget_s=12.0):
-    """Time the fp64 oracle on whole decode steps (all layers) of a sample of
-    sequences, single-threaded BLAS; returns tokens/s and the sample text."""
-    import numpy as np
+def cpu_baseline(wl, src, w, host_seq, budget_s=12.0):
+    """fp64 oracle, single-threaded BLAS, over whole decode steps (all layers)
+    of the first sequences until about ``budget_s`` of CPU time."""
     from threadpoolctl import threadpool_limits
+
     from oracle import attention as A
 
-    seqs = []
+    done = 0
     elapsed = 0.0
     with threadpool_limits(limits=1):
-        b = 0
-        while elapsed < budget_s and b < wl.batch:
-            kk, vv, qs = cache_host_fn(b)
+        while elapsed < budget_s and done < wl.batch:
+            kk, vv, qs = host_seq(done)
             t0 = time.perf_counter()
             for l in range(wl.n_layers):
                 A.layer_decode(src.tolist(), w.tolist(), l, kk, vv, qs[l], [wl.ctx])
             elapsed += time.perf_counter() - t0
-            seqs.append(b)
-            b += 1
-    return {"value": len(seqs) / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(seqs)} of {wl.batch} sequences, full decode step over all "
-                      f"{wl.n_layers} layers at ctx {wl.ctx} ({elapsed:.1f} s, bf16->fp64 "
-                      f"upcast included)"}
+            done += 1
+    return {"value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {wl.batch} sequences, full decode step over all "
+                      f"{wl.n_layers} layers at ctx {wl.ctx}, {elapsed:.1f} s "
+                      f"(bf16->fp64 upcast included)"}
 
 
 def main():
@@ -101,11 +106,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tinyllama_cla2",
                     choices=["tiny_cla2", "tinyllama_cla2", "depthgraft", "cla2_64k"])
+    ap.add_argument("--roofline-passes", type=int, default=3)
+    ap.add_argument("--roofline-only", action="store_true",
+                    help="only the cache-flushed per-launch timing loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path is a "
-              "single-GPU kernel library; multi-GPU sharding is described, not built.",
+              "single-GPU kernel library; sharding across GPUs is described, not built.",
               file=sys.stderr)
         sys.exit(2)
 
@@ -115,90 +123,104 @@ def main():
     src, w, plan, cache, owners = setup(wl)
     L, B = wl.n_layers, wl.batch
     qs = [datagen.decode_q(wl, l, device="cuda") for l in range(L)]
-    new_k = {l: datagen.owner_kv(wl, 1000 + l, device="cuda", ctx=1)[0] for l in owners}
-    new_v = {l: datagen.owner_kv(wl, 1000 + l, device="cuda", ctx=1)[1] for l in owners}
-    # the step's token lands at position ctx-1 (rewritten each step); the
+    new_kv = {l: datagen.owner_kv(wl, 1000 + l, device="cuda", ctx=1) for l in owners}
+    # the step's token lands at position ctx-1 (rewritten every step); the
     # query attends over ctx keys including it
     pos = torch.full((B,), wl.ctx - 1, dtype=torch.int32, device="cuda")
     seq_len = torch.full((B,), wl.ctx, dtype=torch.int32, device="cuda")
     n_splits = K.kvs_decode_splits(plan, B, wl.ctx)
-    ws = torch.empty(K.kvs_decode_workspace_size(plan, B, n_splits), dtype=torch.uint8,
+    ws = torch.zeros(K.kvs_decode_workspace_size(plan, B, n_splits), dtype=torch.uint8,
                      device="cuda")
     outs = [torch.empty((B, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
             for _ in range(L)]
     stream = torch.cuda.current_stream()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(L)] for _ in range(args.steps)]
 
-    def step(i=None):
+    def decode(l):
+        K.kvs_attn_decode(plan, cache, l, qs[l], seq_len, wl.ctx, out=outs[l],
+                          n_splits=n_splits, workspace=ws, stream=stream)
+
+    def step():
         for l in range(L):
-            if l in new_k:
-                K.kvs_append(plan, cache, l, new_k[l], new_v[l], pos, stream=stream)
-            if i is not None:
-                ev[i][l][0].record(stream)
-            K.kvs_attn_decode(plan, cache, l, qs[l], seq_len, wl.ctx, out=outs[l],
-                              n_splits=n_splits, workspace=ws, stream=stream)
-            if i is not None:
-                ev[i][l][1].record(stream)
+            if l in new_kv:
+                K.kvs_append(plan, cache, l, new_kv[l][0], new_kv[l][1], pos, stream=stream)
+            decode(l)
 
-    for _ in range(args.warmup):
-        step()
+    res = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+           "data": "synthetic", "config": describe(wl, src) | {"n_splits": n_splits}}
+
+    if not args.roofline_only:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / args.steps
+        step_bytes = sum(bytes_per_call(wl, src, l) for l in range(L))
+        res |= {"value": B * 1000.0 / ms, "ms_per_step": ms,
+                "step_hbm_gbs": step_bytes / (ms * 1e-3) / 1e9,
+                "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+    # ---- per-launch roofline: cache flushed before every launch
+    flush = torch.ones((FLUSH_BYTES // 4 // 4096, 4096), dtype=torch.float32, device="cuda")
+    single = [l for l in range(L) if int(src[l, 1]) < 0]
+    mixed = [l for l in range(L) if int(src[l, 1]) >= 0]
+    timed = {}
+    for group in (single, mixed):
+        for l in group[:1]:
+            decode(l)                                     # warm the launch path
+        for _ in range(args.roofline_passes):
+            for l in group:
+                flush.sum(dim=0)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                decode(l)
+                e1.record(stream)
+                timed.setdefault(l, []).append((e0, e1))
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
 
-    bytes_per_call = algorithmic_bytes(wl, src)
-    call_ms = [[ev[i][l][0].elapsed_time(ev[i][l][1]) for l in range(L)] for i in range(args.steps)]
-    # dominant kernel: decode launches of single-source layers (the most common
-    # call); for a workload where every layer mixes two sources it is those
-    single = [l for l in range(L) if int(src[l, 1]) < 0] or list(range(L))
-    avg_ms = sum(call_ms[i][l] for i in range(args.steps) for l in single) / (args.steps * len(single))
-    achieved = bytes_per_call[single[0]] / (avg_ms * 1e-3) / 1e9
-    step_bytes = sum(bytes_per_call)
-    res = {
-        "metric": METRIC,
-        "value": B * 1000.0 / ms,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
-        "data": "synthetic",
-        "config": describe(wl) | {"n_splits": n_splits},
-        "step_hbm_gbs": step_bytes / (ms * 1e-3) / 1e9,
-        "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "decode launch (split-K partial + combine), single-source layer",
-                     "bytes_per_launch": bytes_per_call[single[0]],
-                     "avg_launch_us": avg_ms * 1e3},
-    }
-    if not args.no_cpu_baseline:
-        def host_seq(b):
-            kk = {l: datagen_slice(cache_src[l][0], b) for l in owners}
-            vv = {l: datagen_slice(cache_src[l][1], b) for l in owners}
-            return kk, vv, [q[b:b + 1].cpu() for q in qs]
+    def avg_us(layers):
+        d = [e0.elapsed_time(e1) * 1e3 for l in layers for (e0, e1) in timed[l]]
+        return sum(d) / len(d)
 
+    dom = single if single else mixed
+    us = avg_us(dom)
+    nbytes = bytes_per_call(wl, src, dom[0])
+    achieved = nbytes / (us * 1e-6) / 1e9
+    res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                       "kernel": "decode_kernel (split-K partitions + fused merge), "
+                                 + ("single-source layer" if single else "two-source layer"),
+                       "bytes_per_launch": nbytes, "avg_launch_us": us,
+                       "launches": sum(len(timed[l]) for l in dom), "cache": "flushed"}
+    if single and mixed:
+        us2 = avg_us(mixed)
+        b2 = bytes_per_call(wl, src, mixed[0])
+        res["roofline_two_source"] = {"achieved": b2 / (us2 * 1e-6) / 1e9,
+                                      "frac": b2 / (us2 * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                      "bytes_per_launch": b2, "avg_launch_us": us2}
+    del flush
+
+    if not args.roofline_only and not args.no_cpu_baseline:
         log("[bench] cpu baseline")
-        cache_src = {}
+        full = {}
         for l in owners:
             k, v = datagen.owner_kv(wl, l, device="cuda")
-            k[:, wl.ctx - 1:] = new_k[l]
-            v[:, wl.ctx - 1:] = new_v[l]
-            cache_src[l] = (k, v)
+            k[:, wl.ctx - 1:] = new_kv[l][0]
+            v[:, wl.ctx - 1:] = new_kv[l][1]
+            full[l] = (k, v)
 
-        def datagen_slice(t, b):
-            return t[b:b + 1].cpu()
+        def host_seq(b):
+            kk = {l: full[l][0][b:b + 1].cpu() for l in owners}
+            vv = {l: full[l][1][b:b + 1].cpu() for l in owners}
+            return kk, vv, [q[b:b + 1].cpu() for q in qs]
 
         res["cpu_baseline"] = cpu_baseline(wl, src, w, host_seq)
     print(json.dumps(res), flush=True)

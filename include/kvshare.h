@@ -107,7 +107,9 @@ typedef struct {
 
 /* Byte sizes of the caller-allocated device buffers.  Pool layouts (64-token
  * pages; page p of sequence b lives in physical page page_table[b][p]):
- *   dense K pool  [n_slots][n_phys_pages][Hkv][hd/E][64][E]   E = 16 B / elem
+ *   dense K pool  [n_slots][n_phys_pages][Hkv][4][hd/(4E)][16][4][E],
+ *                 E = 16 B / elem: chunk c (E elements) of token t of a page
+ *                 at (((t/16)*(hd/(4E)) + c/4)*64 + 4*(t%16) + c%4)*E
  *   dense V pool  [n_slots][n_phys_pages][Hkv][32][hd][2]     token pairs
  *                 (element (t, d) of a page at (t/2)*hd*2 + d*2 + t%2)
  *   page table    [max_batch][pages_per_seq] int32 in [0, n_phys_pages)
@@ -181,7 +183,9 @@ KVS_API kvs_status kvs_cache_layout(const kvs_plan* plan, kvs_cache_sizes* out);
  * page boundaries. */
 KVS_API kvs_status kvs_decode_splits(const kvs_plan* plan, int32_t batch,
                                      int32_t max_seq_len, int32_t* n_splits);
-/* Workspace bytes kvs_attn_decode needs for (batch, n_splits). */
+/* Workspace bytes kvs_attn_decode needs for (batch, n_splits), n_splits in
+ * [1, 64]: per-partition partial results, maxima and sums (fp32).  Calls
+ * sharing a workspace must not overlap in time. */
 KVS_API kvs_status kvs_decode_workspace_size(const kvs_plan* plan, int32_t batch,
                                              int32_t n_splits, size_t* bytes);
 

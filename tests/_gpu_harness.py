@@ -52,7 +52,10 @@ class Dense:
                             batch, ctx)
         self.plan = K.kvs_share_plan(cfg, self.src, self.w)
         self.cache = K.Cache(self.plan, "cuda", page_perm=page_perm)
-        if nan_fill:   # unwritten cache memory holds NaN patterns
+        if nan_fill == "zero":
+            self.cache.k_pool.zero_()
+            self.cache.v_pool.zero_()
+        elif nan_fill:   # unwritten cache memory holds NaN patterns
             self.cache.k_pool.fill_(0xFF)
             self.cache.v_pool.fill_(0xFF)
         self.owners = datagen.owner_layers(self.src)

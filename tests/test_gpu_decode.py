@@ -118,11 +118,9 @@ def test_append_layout_bit_exact_and_incremental():
     pool bytes sit where the documented page layouts put them."""
     wl = W["tinyllama_cla2"].with_(n_layers=2, n_q_heads=8, n_kv_heads=2)
     B, ctx = 2, 140
-    bulk = Dense(wl, B, ctx, [ctx, ctx], nan_fill=False)
-    inc = Dense(wl, B, ctx, [ctx, ctx], nan_fill=False, append_lens=[0, 0])
+    bulk = Dense(wl, B, ctx, [ctx, ctx], nan_fill="zero")
+    inc = Dense(wl, B, ctx, [ctx, ctx], nan_fill="zero", append_lens=[0, 0])
     k, v = bulk.k[0].cuda(), bulk.v[0].cuda()
-    inc.cache.k_pool.zero_()
-    inc.cache.v_pool.zero_()
     bulk_k = bulk.cache.k_pool.clone()
     for t in range(ctx):
         sp = torch.full((B,), t, dtype=torch.int32, device="cuda")
@@ -140,7 +138,13 @@ def test_append_layout_bit_exact_and_incremental():
             for kvh in range(Hkv):
                 base = _page_offset(pt, b, pos, kvh, hd, Hkv, n_phys, 0)
                 t = pos % 64
-                krow = torch.stack([kp[base + (d // 8) * 512 + t * 8 + d % 8] for d in range(hd)])
+                E, ncq = 8, hd // 32
+
+                def koff(d):
+                    c = d // E
+                    return (((t // 16) * ncq + c // 4) * 64 + 4 * (t % 16) + c % 4) * E + d % E
+
+                krow = torch.stack([kp[base + koff(d)] for d in range(hd)])
                 vrow = torch.stack([vp[base + (t // 2) * hd * 2 + d * 2 + t % 2] for d in range(hd)])
                 assert torch.equal(krow, bulk.k[0][b, pos, kvh])
                 assert torch.equal(vrow, bulk.v[0][b, pos, kvh])
