@@ -134,9 +134,46 @@ extern "C" kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cac
   clear_error();
   kvs_status st = check_layer(plan, layer);
   if (st != KVS_OK) return st;
-  (void)cache; (void)q; (void)n; (void)seq_len; (void)batch; (void)causal; (void)out;
-  (void)out_dtype; (void)stream;
-  return fail(KVS_ERR_UNSUPPORTED, "prefill is not built");
+  const Plan& p = plan->p;
+  if (!cache || !q || !seq_len || !out) return fail(KVS_ERR_ARG, "null argument");
+  if ((st = check_batch(plan, batch)) != KVS_OK) return st;
+  if (n < 1 || n > p.cfg.max_ctx) return fail(KVS_ERR_RANGE, "n out of range");
+  if (out_dtype != KVS_F32 && out_dtype != KVS_BF16) return fail(KVS_ERR_ARG, "bad out_dtype");
+  if (p.cfg.kind != KVS_DENSE || p.cfg.dtype != KVS_BF16)
+    return fail(KVS_ERR_UNSUPPORTED, "prefill runs on dense bf16 caches (bf16 MFMA)");
+  const int32_t group = p.cfg.n_q_heads / p.cfg.n_kv_heads;
+  if (!prefill_shape_supported(p.cfg.head_dim, group))
+    return fail(KVS_ERR_UNSUPPORTED, "no prefill kernel for this head_dim/group size");
+  if (!cache->k_pool || !cache->v_pool || !cache->page_table) return fail(KVS_ERR_ARG, "null cache pool");
+  if (!aligned16(q) || !aligned16(out) || !aligned16(cache->k_pool) || !aligned16(cache->v_pool) ||
+      !aligned4(seq_len) || !aligned4(cache->page_table))
+    return fail(KVS_ERR_ALIGN, "q, out and the pools must be 16-byte aligned");
+  const kvs_layer_info& li = p.layers[layer];
+  PrefillLaunch a;
+  a.k_pool = cache->k_pool;
+  a.v_pool = cache->v_pool;
+  a.page_table = cache->page_table;
+  a.pages_per_seq = p.pages_per_seq;
+  a.n_phys_pages = p.n_phys_pages;
+  a.n_kv_heads = p.cfg.n_kv_heads;
+  a.n_q_heads = p.cfg.n_q_heads;
+  a.head_dim = p.cfg.head_dim;
+  a.slot_stride = (int64_t)p.n_phys_pages * p.cfg.n_kv_heads * kPage * p.cfg.head_dim;
+  a.n_src = li.n_src;
+  a.slot[0] = li.src_slot[0];
+  a.slot[1] = li.src_slot[1];
+  a.weight[0] = li.weight[0];
+  a.weight[1] = li.weight[1];
+  a.q = q;
+  a.n = n;
+  a.seq_len = seq_len;
+  a.max_ctx = p.cfg.max_ctx;
+  a.batch = batch;
+  a.causal = causal != 0;
+  a.scale_log2 = scale_log2(p.cfg.head_dim);
+  a.out = out;
+  a.out_dtype = out_dtype;
+  return hip_status(launch_prefill(a, stream), "prefill launch");
 }
 
 extern "C" kvs_status kvs_append_factorized(const kvs_plan* plan, const kvs_cache* cache,

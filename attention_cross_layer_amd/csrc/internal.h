@@ -83,11 +83,14 @@ struct AppendLaunch {
 };
 int launch_append(const AppendLaunch& a, void* stream);
 
+bool prefill_shape_supported(int32_t head_dim, int32_t group);
+
 struct PrefillLaunch {
   const void* k_pool;
   const void* v_pool;
   const int32_t* page_table;
   int32_t pages_per_seq;
+  int32_t n_phys_pages;
   int32_t n_kv_heads;
   int32_t n_q_heads;
   int32_t head_dim;

@@ -1,0 +1,368 @@
+// Causal (or full) prefill-chunk attention over the shared paged K/V cache,
+// on bf16 MFMA with fp32 accumulation.
+//
+// A chunk of n queries per sequence sits at the last n positions: query i of
+// sequence b is at P = seq_len[b] - n + i and, causal, sees keys 0..P.  The
+// keys of the chunk itself were appended first, so the whole key range comes
+// from the cache of the layer's source slot(s) (CLA page, "Reducing
+// Transformer Key-Value Cache Size with Cross-Layer Attention", Methodology:
+// reusing layers read the source layer's K/V).  A two-source layer reads the
+// DepthGraft mix K~ = w0 K_s0 + w1 K_s1 ("DepthGraft: Structural
+// Regularization through Hierarchical Cross-Layer KV Reconstruction",
+// Abstract), formed in fp32 while a tile is staged and rounded to bf16 for
+// the MFMA.  DepthGraft's owner layers are the only ones that need prefill
+// for all prompt tokens (the Abstract's "prefill early completion").
+//
+// Decomposition (gfx950, v_mfma_f32_32x32x16_bf16; lane l of A/B holds row or
+// column l%32 and k = 8*(l/32)+e; result register r of lane l is row
+// 8*(r/4) + 4*(l/32) + r%4, column l%32):
+//   workgroup = 4 waves sharing one KV head: HW = min(G, 4) query heads x
+//   4/HW blocks of 32 consecutive query positions; each wave owns 32 query
+//   rows of one head.  Per 64-key tile (one cache page):
+//     staging  all 256 threads copy the K page into LDS as [64 keys][hd]
+//              (16-byte chunks XOR-swizzled by key) and the V page as V^T
+//              [hd][64+4 keys]; keys past the sequence end are zeroed (cache
+//              memory there is unwritten).  Registers hold the next tile's
+//              global loads while the current tile is computed; one barrier
+//              per tile (double-buffered LDS).
+//     S^T = K Q^T   16 MFMAs (2 blocks of 32 keys x hd/16 steps): each lane
+//              ends up with 32 scores of one query row (its column).
+//     softmax  online, per query row, in registers; the two lanes of a row
+//              exchange their tile maximum with one cross-half shuffle.
+//     O^T += V^T P^T   the probabilities, rounded to bf16, are the B operand
+//              straight from the S^T registers; the MFMA's k index runs over
+//              keys in the order those registers hold them, and V^T is read
+//              from LDS in the same order.
+//   Work order: workgroups with later query positions (more causal keys)
+//   are dispatched first; the KV head is the fastest-varying index so each
+//   XCD's L2 serves the K/V of one head.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "common.cuh"
+#include "internal.h"
+
+namespace kvs {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+constexpr int kRows = 32;        // query rows per wave
+constexpr int kVRow = 64 + 4;    // V^T row pitch in keys (8-byte aligned, bank-spread)
+
+struct PrefillParams {
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* page_table;
+  int32_t pages_per_seq;
+  int32_t n_phys_pages;
+  int32_t n_kv_heads;
+  int32_t n_q_heads;
+  int64_t slot_stride;  // elements
+  int32_t slot0, slot1;
+  float w0, w1;
+  const uint16_t* q;    // [B][n][Hq][hd]
+  int32_t n;
+  const int32_t* seq_len;
+  int32_t max_ctx;
+  int32_t causal;
+  float scale_log2;
+  void* out;            // [B][n][Hq][hd]
+  int32_t out_bf16;
+  int32_t n_pos_groups; // workgroups along query positions
+  int32_t head_groups;  // G / HW
+};
+
+__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return dev::f32_to_bf16_bits(lo) | (dev::f32_to_bf16_bits(hi) << 16);
+}
+
+// w0*a + w1*b per bf16 element of two 16-byte chunks, rounded back to bf16.
+__device__ __forceinline__ uint4 mix_chunk(const uint4& a, const uint4& b, float w0, float w1) {
+  uint4 r;
+  const uint32_t* pa = &a.x;
+  const uint32_t* pb = &b.x;
+  uint32_t* pr = &r.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = fmaf(w0, dev::bf16_lo(pa[i]), w1 * dev::bf16_lo(pb[i]));
+    const float hi = fmaf(w0, dev::bf16_hi(pa[i]), w1 * dev::bf16_hi(pb[i]));
+    pr[i] = pack_bf16(lo, hi);
+  }
+  return r;
+}
+
+template <int HD, int G, int NSRC>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams a) {
+  constexpr int HW = G < 4 ? G : 4;          // heads per workgroup
+  constexpr int PB = 4 / HW;                 // 32-row position blocks per workgroup
+  constexpr int NCH = HD / 8;                // 16-byte chunks per key row
+  constexpr int NCQ = NCH / 4;
+  constexpr int KS = HD / 16;                // MFMA k-steps over the head dim
+  constexpr int MB = HD / 32;                // 32-dim blocks of O^T
+  constexpr int KCH = 64 * NCH / 256;        // K chunks staged per thread per source
+  constexpr int VCH = KCH;                   // V chunks staged per thread per source
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][64 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][HD * kVRow];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5;                  // k half of the MFMA operands
+  const int col = lane & 31;                 // MFMA column owned by this lane
+
+  // ---- which (sequence, KV head, heads, positions)
+  const int b = blockIdx.y;
+  int x = blockIdx.x;
+  const int kvh = x % a.n_kv_heads;
+  x /= a.n_kv_heads;
+  const int hg = x % a.head_groups;
+  const int pgrp = a.n_pos_groups - 1 - x / a.head_groups;   // late positions first
+  const int head = kvh * G + hg * HW + (wave % HW);
+  const int i0 = (pgrp * PB + wave / HW) * kRows;            // this wave's first row
+  const int n = a.n;
+
+  const int T = min(max(a.seq_len[b], 0), a.max_ctx);
+  const int wg_last_row = min(n, (pgrp + 1) * PB * kRows) - 1;
+  int kend = T;
+  if (a.causal) kend = min(T, T - n + wg_last_row + 1);
+  kend = max(kend, 0);
+  const int n_tiles = (kend + 63) / 64;
+
+  // ---- this lane's query row (MFMA column) and its key limit
+  const int row = i0 + col;
+  const bool row_ok = row < n;
+  const int pos = T - n + row;                               // absolute position
+  const int row_kend = !row_ok ? 0 : (a.causal ? min(T, pos + 1) : T);
+
+  uint4 qreg[KS];
+  {
+    const int qrow = row_ok ? row : (n - 1);                 // stay in bounds
+    const uint16_t* qp = a.q + (((size_t)b * n + qrow) * a.n_q_heads + head) * HD;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qreg[ks] = *reinterpret_cast<const uint4*>(qp + (2 * ks + hh) * 8);
+  }
+
+  const int32_t* pt = a.page_table + (size_t)b * a.pages_per_seq;
+  const int64_t so0 = (int64_t)a.slot0 * a.slot_stride;
+  const int64_t so1 = (int64_t)a.slot1 * a.slot_stride;
+
+  uint4 kst[NSRC][KCH], vst[NSRC][VCH];
+  auto load_tile = [&](int t) {
+    int page = pt[t];
+    if ((unsigned)page >= (unsigned)a.n_phys_pages) page = 0;   // corrupt entry: read page 0, masked below
+    const int64_t tile = ((int64_t)page * a.n_kv_heads + kvh) * (64 * HD);
+#pragma unroll
+    for (int s = 0; s < NSRC; ++s) {
+      const uint16_t* kp = a.k_pool + (s == 0 ? so0 : so1) + tile;
+      const uint16_t* vp = a.v_pool + (s == 0 ? so0 : so1) + tile;
+#pragma unroll
+      for (int u = 0; u < KCH; ++u) kst[s][u] = *reinterpret_cast<const uint4*>(kp + (tid + 256 * u) * 8);
+#pragma unroll
+      for (int u = 0; u < VCH; ++u) vst[s][u] = *reinterpret_cast<const uint4*>(vp + (tid + 256 * u) * 8);
+    }
+  };
+  auto store_tile = [&](int t, int buf) {
+    const int key0 = t * 64;
+    const bool page_ok = (unsigned)pt[t] < (unsigned)a.n_phys_pages;
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+      // cache layout chunk index -> (key, chunk)
+      const int qi = tid + 256 * u;
+      const int j = qi / (NCQ * 64), cc = (qi / 64) % NCQ, k16 = (qi % 64) / 4, qd = qi % 4;
+      const int key = 16 * j + k16, c = 4 * cc + qd;
+      uint4 v = NSRC == 2 ? mix_chunk(kst[0][u], kst[NSRC - 1][u], a.w0, a.w1) : kst[0][u];
+      *reinterpret_cast<uint4*>(&k_lds[buf][key * HD + ((c ^ (key & (NCH - 1))) * 8)]) = v;
+    }
+#pragma unroll
+    for (int u = 0; u < VCH; ++u) {
+      const int qi = tid + 256 * u;
+      const int pair = qi / (HD / 4), d0 = 4 * (qi % (HD / 4));
+      uint4 v = NSRC == 2 ? mix_chunk(vst[0][u], vst[NSRC - 1][u], a.w0, a.w1) : vst[0][u];
+      const int k0 = key0 + 2 * pair;                         // keys k0, k0+1
+      const uint32_t mk = (page_ok && k0 < T ? 0x0000ffffu : 0u) | (page_ok && k0 + 1 < T ? 0xffff0000u : 0u);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&v_lds[buf][0]);
+      dst[((d0 + 0) * kVRow + 2 * pair) / 2] = v.x & mk;
+      dst[((d0 + 1) * kVRow + 2 * pair) / 2] = v.y & mk;
+      dst[((d0 + 2) * kVRow + 2 * pair) / 2] = v.z & mk;
+      dst[((d0 + 3) * kVRow + 2 * pair) / 2] = v.w & mk;
+    }
+  };
+
+  f32x16_t o[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) o[mb] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (n_tiles > 0) load_tile(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    store_tile(t, buf);
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    __syncthreads();
+
+    // ---- S^T = K Q^T: two 32-key blocks
+    f32x16_t s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16_t{};
+      const int key = 32 * kb + col;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int c = 2 * ks + hh;
+        const uint4 kv = *reinterpret_cast<const uint4*>(&k_lds[buf][key * HD + ((c ^ (key & (NCH - 1))) * 8)]);
+        s[kb] = mfma32(kv, qreg[ks], s[kb]);
+      }
+    }
+
+    // ---- online softmax for this lane's query row
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = t * 64 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
+        const float v = key < row_kend ? s[kb][r] * a.scale_log2 : -INFINITY;
+        s[kb][r] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m_run, mt);
+    const float alpha = mn == -INFINITY ? 1.f : dev::fast_exp2(m_run - mn);
+    m_run = mn;
+    float lt = 0.f;
+    uint4 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = s[kb][8 * sh + e];
+          p[e] = v == -INFINITY ? 0.f : dev::fast_exp2(v - mn);
+        }
+        uint4 w;
+        w.x = pack_bf16(p[0], p[1]);
+        w.y = pack_bf16(p[2], p[3]);
+        w.z = pack_bf16(p[4], p[5]);
+        w.w = pack_bf16(p[6], p[7]);
+        // the running sum uses the same bf16-rounded probabilities
+        lt += dev::bf16_lo(w.x) + dev::bf16_hi(w.x) + dev::bf16_lo(w.y) + dev::bf16_hi(w.y) +
+              dev::bf16_lo(w.z) + dev::bf16_hi(w.z) + dev::bf16_lo(w.w) + dev::bf16_hi(w.w);
+        pb[2 * kb + sh] = w;
+      }
+    l_run = fmaf(l_run, alpha, lt);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+
+    // ---- O^T += V^T P^T; step sp covers keys 16sp + 8(e/4) + 4hh + e%4
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int d = 32 * mb + col;
+        const uint16_t* vrow = &v_lds[buf][d * kVRow + 16 * sp + 4 * hh];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
+        o[mb] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[sp], o[mb]);
+      }
+  }
+
+  // ---- normalise and store this lane's row: dims 32mb + 8(r/4) + 4hh + r%4
+  const float l_row = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+  const size_t obase = (((size_t)b * n + row) * a.n_q_heads + head) * HD;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = 32 * mb + 8 * g4 + 4 * hh;
+      const float v0 = o[mb][4 * g4 + 0] * inv, v1 = o[mb][4 * g4 + 1] * inv;
+      const float v2 = o[mb][4 * g4 + 2] * inv, v3 = o[mb][4 * g4 + 3] * inv;
+      if (a.out_bf16) {
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + obase + d) =
+            make_uint2(pack_bf16(v0, v1), pack_bf16(v2, v3));
+      } else {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + obase + d) =
+            make_float4(v0, v1, v2, v3);
+      }
+    }
+}
+
+template <int HD, int G, int NSRC>
+int run_prefill(PrefillParams p, int B, hipStream_t st) {
+  constexpr int HW = G < 4 ? G : 4;
+  constexpr int PB = 4 / HW;
+  p.head_groups = G / HW;
+  p.n_pos_groups = (p.n + PB * kRows - 1) / (PB * kRows);
+  dim3 grid(p.n_pos_groups * p.head_groups * p.n_kv_heads, B);
+  hipLaunchKernelGGL((prefill_kernel<HD, G, NSRC>), grid, dim3(256), 0, st, p);
+  return (int)hipGetLastError();
+}
+
+typedef int (*PrefillFn)(PrefillParams, int, hipStream_t);
+
+template <int HD, int NSRC>
+PrefillFn pick_g(int G) {
+  switch (G) {
+    case 1: return run_prefill<HD, 1, NSRC>;
+    case 2: return run_prefill<HD, 2, NSRC>;
+    case 4: return run_prefill<HD, 4, NSRC>;
+    case 8: return run_prefill<HD, 8, NSRC>;
+    default: return nullptr;
+  }
+}
+
+PrefillFn pick(int hd, int G, int nsrc) {
+  if (hd == 64) return nsrc == 1 ? pick_g<64, 1>(G) : pick_g<64, 2>(G);
+  if (hd == 128) return nsrc == 1 ? pick_g<128, 1>(G) : pick_g<128, 2>(G);
+  return nullptr;
+}
+
+}  // namespace
+
+bool prefill_shape_supported(int32_t head_dim, int32_t group) {
+  return pick(head_dim, group, 1) != nullptr;
+}
+
+int launch_prefill(const PrefillLaunch& a, void* stream) {
+  PrefillFn fn = pick(a.head_dim, a.n_q_heads / a.n_kv_heads, a.n_src);
+  if (!fn) return (int)hipErrorInvalidValue;
+  PrefillParams p;
+  p.k_pool = static_cast<const uint16_t*>(a.k_pool);
+  p.v_pool = static_cast<const uint16_t*>(a.v_pool);
+  p.page_table = a.page_table;
+  p.pages_per_seq = a.pages_per_seq;
+  p.n_phys_pages = a.n_phys_pages;
+  p.n_kv_heads = a.n_kv_heads;
+  p.n_q_heads = a.n_q_heads;
+  p.slot_stride = a.slot_stride;
+  p.slot0 = a.slot[0];
+  p.slot1 = a.n_src == 2 ? a.slot[1] : a.slot[0];
+  p.w0 = a.weight[0];
+  p.w1 = a.n_src == 2 ? a.weight[1] : 0.f;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.n = a.n;
+  p.seq_len = a.seq_len;
+  p.max_ctx = a.max_ctx;
+  p.causal = a.causal;
+  p.scale_log2 = a.scale_log2;
+  p.out = a.out;
+  p.out_bf16 = a.out_dtype == KVS_BF16;
+  return fn(p, a.batch, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace kvs
