@@ -94,7 +94,48 @@ extern "C" kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cac
     return fail(KVS_ERR_ALIGN, "q, out and workspace must be 16-byte aligned");
   const kvs_layer_info& li = p.layers[layer];
   const int32_t group = p.cfg.n_q_heads / p.cfg.n_kv_heads;
-  if (p.cfg.kind == KVS_FACTORIZED) return fail(KVS_ERR_UNSUPPORTED, "factorized decode is not built");
+  if (p.cfg.kind == KVS_FACTORIZED) {
+    if (!cache->ck_pool || !cache->cv_pool || !cache->dk_pool || !cache->dv_pool || !cache->sk_pool ||
+        !cache->sv_pool || !cache->rank_pool || !cache->page_table || !cache->basis_k ||
+        !cache->basis_v || !cache->ubasis_k || !cache->ubasis_v)
+      return fail(KVS_ERR_ARG, "null factorized cache buffer");
+    if (!aligned16(cache->ck_pool) || !aligned16(cache->cv_pool) || !aligned16(cache->dk_pool) ||
+        !aligned16(cache->dv_pool) || !aligned16(cache->basis_k) || !aligned16(cache->basis_v) ||
+        !aligned16(cache->ubasis_k) || !aligned16(cache->ubasis_v) || !aligned4(cache->page_table))
+      return fail(KVS_ERR_ALIGN, "factorized buffers must be 16-byte aligned");
+    FactDecodeLaunch f;
+    f.ck_pool = cache->ck_pool;
+    f.cv_pool = cache->cv_pool;
+    f.dk_pool = cache->dk_pool;
+    f.dv_pool = cache->dv_pool;
+    f.sk_pool = cache->sk_pool;
+    f.sv_pool = cache->sv_pool;
+    f.rank_pool = cache->rank_pool;
+    f.basis_k = cache->basis_k;
+    f.basis_v = cache->basis_v;
+    f.ubasis_k = cache->ubasis_k;
+    f.ubasis_v = cache->ubasis_v;
+    f.page_table = cache->page_table;
+    f.pages_per_seq = p.pages_per_seq;
+    f.n_phys_pages = p.n_phys_pages;
+    f.n_kv_heads = p.cfg.n_kv_heads;
+    f.n_q_heads = p.cfg.n_q_heads;
+    f.head_dim = p.cfg.head_dim;
+    f.basis_rank = p.cfg.basis_rank;
+    f.resid_rank_max = p.cfg.resid_rank_max;
+    f.coef_slot = li.src_slot[0];
+    f.layer = layer;
+    f.q = q;
+    f.seq_len = seq_len;
+    f.max_ctx = p.cfg.max_ctx;
+    f.batch = batch;
+    f.n_splits = n_splits;
+    f.scale_log2 = scale_log2(p.cfg.head_dim);
+    f.ws = static_cast<float*>(workspace);
+    f.out = out;
+    f.out_dtype = out_dtype;
+    return hip_status(launch_fact_decode(f, stream), "factorized decode launch");
+  }
   if (!cache->k_pool || !cache->v_pool || !cache->page_table) return fail(KVS_ERR_ARG, "null cache pool");
   if (!aligned16(cache->k_pool) || !aligned16(cache->v_pool) || !aligned4(cache->page_table))
     return fail(KVS_ERR_ALIGN, "pools must be 16-byte aligned");
@@ -184,11 +225,51 @@ extern "C" kvs_status kvs_append_factorized(const kvs_plan* plan, const kvs_cach
   clear_error();
   kvs_status st = check_layer(plan, layer);
   if (st != KVS_OK) return st;
-  (void)cache; (void)ck; (void)cv; (void)dk; (void)dv; (void)sk; (void)sv; (void)rank; (void)n;
-  (void)start_pos; (void)batch; (void)stream;
-  return fail(KVS_ERR_UNSUPPORTED, "factorized cache is not built");
+  const Plan& p = plan->p;
+  if (p.cfg.kind != KVS_FACTORIZED) return fail(KVS_ERR_ARG, "kvs_append_factorized needs a factorized plan");
+  if (!cache || !dk || !dv || !sk || !sv || !start_pos) return fail(KVS_ERR_ARG, "null argument");
+  if (!cache->ck_pool || !cache->cv_pool || !cache->dk_pool || !cache->dv_pool || !cache->sk_pool ||
+      !cache->sv_pool || !cache->rank_pool || !cache->page_table)
+    return fail(KVS_ERR_ARG, "null cache pool");
+  if ((st = check_batch(plan, batch)) != KVS_OK) return st;
+  if (n < 0 || n > p.cfg.max_ctx) return fail(KVS_ERR_RANGE, "n out of range");
+  const kvs_layer_info& li = p.layers[layer];
+  if ((ck == nullptr) != (cv == nullptr)) return fail(KVS_ERR_ARG, "give both ck and cv, or neither");
+  if (ck && !li.owns_kv)
+    return fail(KVS_ERR_NOT_SOURCE, "layer " + std::to_string(layer) + " does not own its pair's coefficients");
+  if ((ck && (!aligned16(ck) || !aligned16(cv))) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned16(cache->ck_pool) || !aligned16(cache->cv_pool) || !aligned16(cache->dk_pool) ||
+      !aligned16(cache->dv_pool))
+    return fail(KVS_ERR_ALIGN, "coefficients, codes and pools must be 16-byte aligned");
+  if (!aligned4(start_pos) || !aligned4(cache->page_table) || ((uintptr_t)sk & 1) || ((uintptr_t)sv & 1))
+    return fail(KVS_ERR_ALIGN, "misaligned scale or int32 array");
+  if (n == 0) return KVS_OK;
+  FactAppendLaunch a;
+  a.ck_pool = cache->ck_pool;
+  a.cv_pool = cache->cv_pool;
+  a.dk_pool = cache->dk_pool;
+  a.dv_pool = cache->dv_pool;
+  a.sk_pool = cache->sk_pool;
+  a.sv_pool = cache->sv_pool;
+  a.rank_pool = cache->rank_pool;
+  a.page_table = cache->page_table;
+  a.pages_per_seq = p.pages_per_seq;
+  a.n_phys_pages = p.n_phys_pages;
+  a.n_kv_heads = p.cfg.n_kv_heads;
+  a.basis_rank = p.cfg.basis_rank;
+  a.resid_rank_max = p.cfg.resid_rank_max;
+  a.coef_slot = ck ? li.src_slot[0] : -1;
+  a.layer = layer;
+  a.ck = ck;
+  a.cv = cv;
+  a.dk = dk;
+  a.dv = dv;
+  a.sk = sk;
+  a.sv = sv;
+  a.rank = rank;
+  a.n = n;
+  a.start_pos = start_pos;
+  a.batch = batch;
+  a.max_ctx = p.cfg.max_ctx;
+  return hip_status(launch_fact_append(a, stream), "factorized append launch");
 }
-
-namespace kvs {
-bool fact_shape_supported(int32_t, int32_t, int32_t, int32_t) { return false; }
-}  // namespace kvs

@@ -100,7 +100,7 @@ __device__ __forceinline__ uint4 mix_chunk(const uint4& a, const uint4& b, float
 }
 
 template <int HD, int G, int NSRC>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams a) {
+__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
   constexpr int HW = G < 4 ? G : 4;          // heads per workgroup
   constexpr int PB = 4 / HW;                 // 32-row position blocks per workgroup
   constexpr int NCH = HD / 8;                // 16-byte chunks per key row

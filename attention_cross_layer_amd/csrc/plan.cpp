@@ -189,8 +189,9 @@ extern "C" kvs_status kvs_decode_splits(const kvs_plan* plan, int32_t batch, int
   return KVS_OK;
 }
 
-// Workspace: per-partition partial results [B][Hq][S][hd] fp32, then the
-// running maxima and sums [B][Hq][S] fp32 each.
+// Workspace: per-partition partial results [B][Hq][S][W] fp32 (W = hd for a
+// dense plan, R + Rmax coefficients for a factorized one), then the running
+// maxima and sums [B][Hq][S] fp32 each.
 extern "C" kvs_status kvs_decode_workspace_size(const kvs_plan* plan, int32_t batch,
                                                 int32_t n_splits, size_t* bytes) {
   clear_error();
@@ -198,7 +199,9 @@ extern "C" kvs_status kvs_decode_workspace_size(const kvs_plan* plan, int32_t ba
   if (batch < 1 || batch > plan->p.cfg.max_batch) return fail(KVS_ERR_RANGE, "batch out of range");
   if (n_splits < 1 || n_splits > max_decode_splits()) return fail(KVS_ERR_RANGE, "n_splits out of range");
   const kvs_config& c = plan->p.cfg;
-  *bytes = size_t(batch) * c.n_q_heads * n_splits * (c.head_dim + 2) * sizeof(float);
+  // a factorized plan's partial results live in the R + Rmax coefficient space
+  const int32_t width = c.kind == KVS_DENSE ? c.head_dim : c.basis_rank + c.resid_rank_max;
+  *bytes = size_t(batch) * c.n_q_heads * n_splits * (width + 2) * sizeof(float);
   return KVS_OK;
 }
 

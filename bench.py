@@ -99,6 +99,81 @@ def cpu_baseline(wl, src, w, host_seq, budget_s=12.0):
                       f"(bf16->fp64 upcast included)"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(n, T, n_q_heads, hd):
+    """Algorithmic FLOPs of a causal chunk: only unmasked (query, key) pairs,
+    QK^T and PV each 2*hd per pair."""
+    pairs = n * (T - n) + n * (n + 1) // 2
+    return pairs * 4 * hd * n_q_heads
+
+
+def prefill_main(args):
+    """DepthGraft prefill: the second 4096-token chunk of an 8192-token prompt
+    (queries at 4096..8191, causal), batch 1, over the 16 owner layers (the
+    deeper layers own no cache entries, so prompt tokens need not run them).
+    A step appends the chunk's K/V to each owner layer and runs its
+    prefill-chunk attention."""
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only", file=sys.stderr)
+        sys.exit(2)
+    wl = datagen.WORKLOADS["depthgraft"].with_(batch=1)
+    n, T = wl.prefill_n, wl.ctx
+    torch.cuda.set_device(0)
+    log(f"[bench] setting up {wl.name} prefill chunk n={n} at offset {T - n}")
+    src, w, plan, cache, owners = setup(wl)
+    qs = {l: datagen.prefill_q(wl, l, n, device="cuda") for l in owners}
+    chunk = {l: datagen.owner_kv(wl, l, device="cuda") for l in owners}
+    chunk = {l: (kv[0][:, T - n:].contiguous(), kv[1][:, T - n:].contiguous()) for l, kv in chunk.items()}
+    start = torch.full((1,), T - n, dtype=torch.int32, device="cuda")
+    seq_len = torch.full((1,), T, dtype=torch.int32, device="cuda")
+    outs = {l: torch.empty((1, n, wl.n_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+            for l in owners}
+    stream = torch.cuda.current_stream()
+    ev = {l: [] for l in owners}
+
+    def step(record=False):
+        for l in owners:
+            K.kvs_append(plan, cache, l, chunk[l][0], chunk[l][1], start, stream=stream)
+            if record:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            K.kvs_attn_prefill_chunk(plan, cache, l, qs[l], seq_len, causal=True, out=outs[l],
+                                     stream=stream)
+            if record:
+                e1.record(stream)
+                ev[l].append((e0, e1))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step(record=True)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    us = sum(e0.elapsed_time(e1) for l in owners for (e0, e1) in ev[l]) * 1e3 / (
+        args.steps * len(owners))
+    flops = prefill_flops(n, T, wl.n_q_heads, wl.head_dim)
+    achieved = flops / (us * 1e-6) / 1e12
+    res = {"metric": "shared-KV prefill chunk attn: prefill tokens/s and MFMA utilisation",
+           "value": n * 1000.0 / ms, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "depthgraft_prefill_chunk", "owner_layers": len(owners),
+                      "batch": 1, "chunk": n, "ctx": T, "causal": True,
+                      "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads,
+                      "head_dim": wl.head_dim},
+           "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                        "traffic": None, "kernel": "prefill_kernel (bf16 MFMA, causal)",
+                        "flops_per_launch": flops, "avg_launch_us": us}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,7 +185,11 @@ def main():
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the cache-flushed per-launch timing loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time the DepthGraft causal prefill chunk instead of decode")
     args = ap.parse_args()
+    if args.prefill:
+        return prefill_main(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path is a "
               "single-GPU kernel library; sharding across GPUs is described, not built.",

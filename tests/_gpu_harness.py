@@ -91,3 +91,90 @@ class Dense:
         q = self.q(layer) if q is None else q
         return A.layer_decode(self.src.tolist(), self.w.tolist(), layer, self.k, self.v, q,
                               self.lens.tolist())
+
+
+class Factorized:
+    """A factorized shared cache (pair basis + per-layer int8 residual),
+    populated through kvs_append_factorized; bases copied into the cache's
+    basis buffers."""
+
+    def __init__(self, wl: datagen.Workload, batch: int, ctx: int, lens, junk=True,
+                 dev_gen="cpu", rank_override=None, scale_zero=False):
+        self.wl, self.batch, self.ctx = wl, batch, ctx
+        self.src, self.w = datagen.share_map(wl)
+        cfg = K.make_config(wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, "bf16", batch,
+                            ctx, kind=K.KVS_FACTORIZED, basis_rank=wl.basis_rank,
+                            resid_rank_max=wl.resid_rank_max)
+        self.plan = K.kvs_share_plan(cfg, self.src, self.w)
+        self.cache = c = K.Cache(self.plan, "cuda")
+        for t in (c.ck_pool, c.cv_pool, c.sk_pool, c.sv_pool, c.rank_pool, c.dk_pool, c.dv_pool):
+            t.fill_(0xFF)           # unwritten memory: NaN patterns, rank 255, codes -1
+        self.lens = torch.tensor(lens, dtype=torch.int32)
+        self.seq_len = self.lens.cuda()
+        Hkv, R, Rm, hd = wl.n_kv_heads, wl.basis_rank, wl.resid_rank_max, wl.head_dim
+        n_slots = c.sizes.n_slots
+        self.rank = (datagen.token_ranks(wl, device=dev_gen, batch=batch, ctx=ctx)
+                     if rank_override is None else rank_override).cpu()
+        bk_all = c.basis_k.view(torch.bfloat16).view(n_slots, Hkv, R, hd)
+        bv_all = c.basis_v.view(torch.bfloat16).view(n_slots, Hkv, R, hd)
+        uk_all = c.ubasis_k.view(torch.bfloat16).view(wl.n_layers, Hkv, Rm, hd)
+        uv_all = c.ubasis_v.view(torch.bfloat16).view(wl.n_layers, Hkv, Rm, hd)
+        self.coef, self.basis, self.resid, self.ubasis = {}, {}, {}, {}
+        owners = datagen.owner_layers(self.src)
+        for l in range(wl.n_layers):
+            pair = int(self.src[l, 0])
+            if l in owners:
+                ck, cv = datagen.pair_coeffs(wl, pair // 2, device=dev_gen, batch=batch, ctx=ctx)
+                bk, bv = datagen.pair_basis(wl, pair // 2, device=dev_gen)
+                slot = owners.index(l)
+                bk_all[slot].copy_(bk)
+                bv_all[slot].copy_(bv)
+                self.coef[l] = (ck.cpu(), cv.cpu())
+                self.basis[l] = (bk.cpu(), bv.cpu())
+            uk, uv = datagen.layer_residual_basis(wl, l, device=dev_gen)
+            uk_all[l].copy_(uk)
+            uv_all[l].copy_(uv)
+            dk, dv, sk, sv = datagen.layer_residual(wl, l, self.rank.to(dev_gen), device=dev_gen,
+                                                    junk_beyond_rank=junk)
+            if scale_zero:
+                sk, sv = torch.zeros_like(sk), torch.zeros_like(sv)
+            self.resid[l] = (dk.cpu(), dv.cpu(), sk.cpu(), sv.cpu())
+            self.ubasis[l] = (uk.cpu(), uv.cpu())
+            for b in range(batch):
+                n = int(self.lens[b])
+                if n == 0:
+                    continue
+                sp = torch.full((batch,), ctx, dtype=torch.int32)
+                sp[b] = 0
+                coefs = self.coef.get(l)
+                K.kvs_append_factorized(
+                    self.plan, self.cache, l,
+                    None if coefs is None else coefs[0][:, :n].contiguous().cuda(),
+                    None if coefs is None else coefs[1][:, :n].contiguous().cuda(),
+                    dk[:, :n].contiguous().cuda(), dv[:, :n].contiguous().cuda(),
+                    sk[:, :n].contiguous().cuda(), sv[:, :n].contiguous().cuda(),
+                    self.rank[:, :n].contiguous().cuda() if l == 0 else None, sp.cuda())
+        torch.cuda.synchronize()
+
+    def q(self, layer):
+        return datagen.decode_q(self.wl, layer, batch=self.batch)
+
+    def decode(self, layer, q=None, n_splits=0, out_dtype=torch.float32):
+        q = self.q(layer) if q is None else q
+        return K.kvs_attn_decode(self.plan, self.cache, layer, q.cuda(), self.seq_len,
+                                 int(self.lens.max()), n_splits=n_splits, out_dtype=out_dtype)
+
+    def kv(self, layer, b0=0, b1=None):
+        """Oracle reconstruction of layer's K, V (float64) for sequences b0..b1."""
+        pair = int(self.src[layer, 0])
+        ck, cv = (x[b0:b1] for x in self.coef[pair])
+        bk, bv = self.basis[pair]
+        dk, dv, sk, sv = (x[b0:b1] for x in self.resid[layer])
+        uk, uv = self.ubasis[layer]
+        r = self.rank[b0:b1]
+        return A.factorized_kv(ck, bk, sk, dk, uk, r), A.factorized_kv(cv, bv, sv, dv, uv, r)
+
+    def oracle_decode(self, layer, q=None):
+        q = self.q(layer) if q is None else q
+        k, v = self.kv(layer)
+        return A.attend_decode(q, k, v, self.lens.tolist())
