@@ -34,6 +34,14 @@ __device__ __forceinline__ float dpp(float x) {
                                                     ROW_MASK, 0xf, false));
 }
 
+// x + (x from the lane CTRL selects), for controls under which every lane has
+// a source (quad_perm, row_half_mirror, row_ror): written as a bound_ctrl
+// mov_dpp so the compiler folds it into a single v_add_f32_dpp.
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float x) {
+  return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xf, 0xf, true));
+}
+
 // Max over the 64 lanes, returned to every lane (uniform).
 __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(x, dpp<0xB1>(x));        // quad_perm [1,0,3,2]

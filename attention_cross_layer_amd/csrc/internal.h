@@ -12,6 +12,18 @@
 namespace kvs {
 
 constexpr int kPage = 64;   // tokens per page == keys per decode tile
+// Lanes that share one key's dot product in the decode; it fixes the K page
+// layout [kWays][NCH/kWays][64/kWays][kWays][E] (E elements per 16 bytes,
+// NCH = 16-byte chunks per key row): chunk c of token t sits at
+// (((t / (64/kWays)) * (NCH/kWays) + c / kWays) * 64 + (t % (64/kWays)) * kWays
+//  + c % kWays) * E.
+constexpr int kWays = 8;
+
+// Element offset of chunk c (E elements) of token t within a K page.
+inline constexpr int k_chunk_offset(int t, int c, int nch, int e) {
+  return (((t / (kPage / kWays)) * (nch / kWays) + c / kWays) * kPage + (t % (kPage / kWays)) * kWays +
+          c % kWays) * e;
+}
 
 struct Plan {
   kvs_config cfg;

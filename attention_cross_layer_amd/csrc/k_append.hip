@@ -4,11 +4,11 @@
 // new K/V, the others reuse it), so the pools hold source layers only.
 //
 // Page layouts (64 tokens per page, per KV head):
-//   K  [4][NCQ][16][4][E]  E = elements per 16 bytes, NCQ = hd/(4E): chunk
-//                          c = 4*cc + qd of token t = 16*j + k16 sits at
-//                          ((j*NCQ + cc)*64 + 4*k16 + qd)*E, so the decode's
-//                          lane 4*k16 + qd loads one contiguous 1 KiB per
-//                          (j, cc) and holds a quarter of 16 keys' rows
+//   K  [8][NCW][8][8][E]   E = elements per 16 bytes, NCW = hd/(8E): chunk
+//                          c = 8*cc + w of token t = 8*j + k8 sits at
+//                          ((j*NCW + cc)*64 + 8*k8 + w)*E, so the decode's
+//                          lane 8*k8 + w loads one contiguous 1 KiB per
+//                          (j, cc) and holds an eighth of 8 keys' rows
 //   V  [32][hd][2]         token pairs: element (t, d) at (t/2)*hd*2 + d*2 + t%2
 // One thread moves one 16-byte chunk of the input row; byte copy, no
 // arithmetic on the values.
@@ -42,8 +42,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendLaunch a) {
   const size_t tile = ((size_t)page * a.n_kv_heads + kvh) * kPage * hd + a.slot_offset;
   const size_t src = (((size_t)b * a.n + i) * a.n_kv_heads + kvh) * hd + (size_t)c * E;
 
-  const int ncq = nch / 4;
-  const size_t kdst = ((size_t)((t >> 4) * ncq + (c >> 2)) * kPage + (t & 15) * 4 + (c & 3)) * E;
+  const size_t kdst = (size_t)k_chunk_offset(t, c, nch, E);
   const uint4 kv = *reinterpret_cast<const uint4*>(static_cast<const T*>(a.k) + src);
   *reinterpret_cast<uint4*>(static_cast<T*>(a.k_pool) + tile + kdst) = kv;
 

@@ -1,5 +1,5 @@
-// Split-K decode attention over a shared (paged, source-only) K/V cache, with
-// the merge of the split-K partitions fused into the same launch.
+// Split-K decode attention over a shared (paged, source-only) K/V cache, and
+// the merge of the split-K partitions.
 //
 // One decode query per (sequence, q head) attends over keys 0..seq_len-1 of
 // the layer's source slot(s): the CLA page ("Reducing Transformer Key-Value
@@ -18,14 +18,14 @@
 //   head are served by the same pass, so each cached tile is read from HBM
 //   once per (sequence, KV head), i.e. once for the whole query group.
 //   Per page, per wave:
-//     QK   four lanes share a key: lane 4*k16 + qd holds, in registers for
-//          the whole launch, the query chunks 4*cc + qd (E elements = 16
-//          bytes each) of all G heads.  Pass j (0..3) scores keys 16j + k16:
+//     QK   eight lanes share a key: lane 8*k8 + w holds, in registers for
+//          the whole launch, the query chunks 8*cc + w (E elements = 16
+//          bytes each) of all G heads.  Pass j (0..7) scores keys 8j + k8:
 //          the K page layout puts each (j, cc) slice of 64 lanes x 16 bytes
 //          in one contiguous 1 KiB load; partial dot products
 //          (v_dot2c_f32_bf16: bf16 x bf16 products, fp32 accumulation) are
-//          completed by two quad_perm DPP adds.  Lane qd then keeps the
-//          scores of pass qd, i.e. key 16*qd + k16.
+//          completed by two quad_perm DPP adds and one ds_swizzle (xor 4).
+//          Lane w then keeps the scores of pass w, i.e. key 8*w + k8.
 //     softmax  per-head wave max over DPP, online rescaling; probabilities
 //          are rounded to bf16 for the PV products and the running sum uses
 //          the same rounded values.
@@ -33,9 +33,9 @@
 //          load holds 4 dims x 2 keys; lane l owns 4 dims and every NPH-th
 //          pair, each dword feeding v_dot2c_f32_bf16 with the pair's two
 //          probabilities (read from LDS).
-//   The next page's K is requested as soon as the scores are done and its V
-//   as soon as the PV products are done, so loads overlap the other half of
-//   the page's work.
+//   A page's K and V are requested together; the scores wait only for K.
+//   Loads of other pages overlap through the other waves on the CU (a
+//   register double buffer of whole pages measured slower: it spills).
 //   Merge: the 4 waves' (O, m, l) meet in LDS.  With S = 1 the workgroup
 //   writes the normalised output.  Otherwise it writes its partition to the
 //   workspace and a small merge kernel on the same stream combines the S
@@ -193,9 +193,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
   constexpr int NPH = 64 / NQ;       // pair phases
   constexpr int PPL = 32 / NPH;      // pairs per lane per page
 
-  constexpr int NCQ = NCH / 4;       // chunks of a key row per lane (a quarter)
+  constexpr int NCW = NCH / kWays;   // chunks of a key row per lane (an eighth)
 
-  __shared__ Pair p_lds[4][32 * G];
+  // probabilities of key pair i, head h at i * PSTR + h; the padded row stride
+  // spreads the 32 pairs over the LDS banks
+  constexpr int PSTR = G + 2;
+  __shared__ Pair p_lds[4][32 * PSTR];
   __shared__ float mrg_o[4][G][HD];
   __shared__ float mrg_m[4][G];
   __shared__ float mrg_l[4][G];
@@ -209,22 +212,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
   const int b = blockIdx.z;
   const int S = a.n_splits;
 
-  // QK lane roles: 4 lanes share a key; lane (k16, qd) = 4*k16 + qd holds the
-  // query chunks 4*cc + qd of every head in registers for the whole launch.
-  const int qd = lane & 3;
-  const int k16 = lane >> 2;
-  uint4 qreg[G][NCQ];
+  // QK lane roles: 8 lanes share a key; lane (k8, way) = 8*k8 + way holds the
+  // query chunks 8*cc + way of every head in registers for the whole launch.
+  const int way = lane & (kWays - 1);
+  const int k8 = lane >> 3;
+  uint4 qreg[G][NCW];
   {
     const uint4* qsrc = reinterpret_cast<const uint4*>(
         a.q + ((size_t)b * a.n_q_heads + (size_t)kvh * G) * HD * sizeof(T));
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int cc = 0; cc < NCQ; ++cc) qreg[h][cc] = qsrc[h * NCH + 4 * cc + qd];
+      for (int cc = 0; cc < NCW; ++cc) qreg[h][cc] = qsrc[h * NCH + kWays * cc + way];
   }
-  // after the quad reduction each lane keeps the scores of one key of the
-  // page: pass qd, i.e. key 16*qd + k16
-  const int my_key = 16 * qd + k16;
+  // after the 8-lane reduction each lane keeps the scores of one key of the
+  // page: pass `way`, i.e. key 8*way + k8
+  const int my_key = 8 * way + k8;
 
   const int n_keys = clamp_len(a.seq_len[b], a.max_ctx);
   const int n_pages = (n_keys + kPage - 1) / kPage;
@@ -268,38 +271,32 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
     }
   };
 
-  for (int pg = next_page(pb + wave); pg < pe; pg = next_page(pg + 4)) {
-    // both halves of the page are requested up front; the scores wait only
-    // for K, while V is still in flight
-    uint4 kr[NSRC][NCH];
-    uint4 vr[NSRC][PPL];
-    {
-      const T* kt[NSRC];
-      const T* vt[NSRC];
-      tiles(pg, kt, vt);
-      load_k<T, HD, NSRC>(kr, kt, lane);
-      load_v<T, HD, NSRC, PPL, NPH, DPL>(vr, vt, ph, quad);
-    }
-
-    // ---- scores: pass j covers keys 16j..16j+15, one quarter of the head
-    // dim per lane; the quad_perm DPP adds complete the dot products
+  // One page: scores, online softmax and P V for the K/V already loaded in
+  // (kr, vr).
+  auto compute = [&](int pg, uint4 (&kr)[NSRC][NCH], uint4 (&vr)[NSRC][PPL]) {
+    // ---- scores: pass j covers keys 8j..8j+7, an eighth of the head dim
+    // per lane; quad_perm and row_half_mirror DPP adds complete the dot
+    // products across the 8 lanes of a key
     const int nvalid = n_keys - pg * kPage;   // >= 1
     float sc[G];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kWays; ++j) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-        for (int cc = 0; cc < NCQ; ++cc) {
-          d0 = chunk_dot(qreg[h][cc], kr[0][j * NCQ + cc], d0, T());
-          if (NSRC == 2) d1 = chunk_dot(qreg[h][cc], kr[NSRC - 1][j * NCQ + cc], d1, T());
+        for (int cc = 0; cc < NCW; ++cc) {
+          d0 = chunk_dot(qreg[h][cc], kr[0][j * NCW + cc], d0, T());
+          if (NSRC == 2) d1 = chunk_dot(qreg[h][cc], kr[NSRC - 1][j * NCW + cc], d1, T());
         }
         float s = (NSRC == 2) ? fmaf(a.w0, d0, a.w1 * d1) : d0;
-        s += dev::dpp<0xB1>(s);   // quad_perm [1,0,3,2]
-        s += dev::dpp<0x4E>(s);   // quad_perm [2,3,0,1]
+        s = dev::add_dpp<0xB1>(s);    // quad_perm [1,0,3,2]
+        s = dev::add_dpp<0x4E>(s);    // quad_perm [2,3,0,1]
+        // the other quad of the 8: lane ^ 4 through ds_swizzle (bitmask mode,
+        // xor 4), which keeps the VALU free
+        s += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(s), (4 << 10) | 0x1f));
         if (j == 0) sc[h] = s;
-        else sc[h] = (qd == j) ? s : sc[h];
+        else sc[h] = (way == j) ? s : sc[h];
       }
     }
     const bool key_ok = my_key < nvalid;
@@ -314,7 +311,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
       const float alpha = dev::fast_exp2(m[h] - mn);
       m[h] = mn;
       float used;
-      store_prob(pl, (my_key >> 1) * G + h, my_key & 1, dev::fast_exp2(sc[h] - mn), used);
+      store_prob(pl, (my_key >> 1) * PSTR + h, my_key & 1, dev::fast_exp2(sc[h] - mn), used);
       lsum[h] = fmaf(lsum[h], alpha, used);
 #pragma unroll
       for (int s = 0; s < NSRC; ++s)
@@ -335,12 +332,28 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
       const int i = ph + NPH * j;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const Pair pp = pl[i * G + h];
+        const Pair pp = pl[i * PSTR + h];
 #pragma unroll
         for (int s = 0; s < NSRC; ++s) pair_fma(acc[s][h], pp, vr[s][j], T());
       }
     }
     __builtin_amdgcn_wave_barrier();
+  };
+  auto load = [&](int pg, uint4 (&kr)[NSRC][NCH], uint4 (&vr)[NSRC][PPL]) {
+    const T* kt[NSRC];
+    const T* vt[NSRC];
+    tiles(pg, kt, vt);
+    load_k<T, HD, NSRC>(kr, kt, lane);
+    load_v<T, HD, NSRC, PPL, NPH, DPL>(vr, vt, ph, quad);
+  };
+
+  for (int pg = next_page(pb + wave); pg < pe; pg = next_page(pg + 4)) {
+    // both halves of the page are requested up front; the scores wait only
+    // for K, while V is still in flight
+    uint4 kr[NSRC][NCH];
+    uint4 vr[NSRC][PPL];
+    load(pg, kr, vr);
+    compute(pg, kr, vr);
   }
 
   // ---- this wave's (O, m, l) to LDS

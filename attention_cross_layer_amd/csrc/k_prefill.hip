@@ -104,7 +104,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
   constexpr int HW = G < 4 ? G : 4;          // heads per workgroup
   constexpr int PB = 4 / HW;                 // 32-row position blocks per workgroup
   constexpr int NCH = HD / 8;                // 16-byte chunks per key row
-  constexpr int NCQ = NCH / 4;
   constexpr int KS = HD / 16;                // MFMA k-steps over the head dim
   constexpr int MB = HD / 32;                // 32-dim blocks of O^T
   constexpr int KCH = 64 * NCH / 256;        // K chunks staged per thread per source
@@ -178,8 +177,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
     for (int u = 0; u < KCH; ++u) {
       // cache layout chunk index -> (key, chunk)
       const int qi = tid + 256 * u;
-      const int j = qi / (NCQ * 64), cc = (qi / 64) % NCQ, k16 = (qi % 64) / 4, qd = qi % 4;
-      const int key = 16 * j + k16, c = 4 * cc + qd;
+      constexpr int NCW = NCH / kWays, KPP = 64 / kWays;   // chunks per lane, keys per pass
+      const int j = qi / (NCW * 64), cc = (qi / 64) % NCW, kk = (qi % 64) / kWays, w = qi % kWays;
+      const int key = KPP * j + kk, c = kWays * cc + w;
       uint4 v = NSRC == 2 ? mix_chunk(kst[0][u], kst[NSRC - 1][u], a.w0, a.w1) : kst[0][u];
       *reinterpret_cast<uint4*>(&k_lds[buf][key * HD + ((c ^ (key & (NCH - 1))) * 8)]) = v;
     }

@@ -166,11 +166,12 @@ extern "C" kvs_status kvs_cache_layout(const kvs_plan* plan, kvs_cache_sizes* ou
 }
 
 // Split-K choice.  A decode launch has one 4-wave workgroup per (partition,
-// KV head, sequence).  Aim for kTargetGroups workgroups (two per CU on the
+// KV head, sequence).  Aim for kTargetGroups workgroups (one per CU on the
 // 256-CU MI355X) while keeping at least 4 pages (one per wave) per
-// partition; at most max_decode_splits() partitions (the fused merge keeps
-// one weight per partition in LDS).
-static const int32_t kTargetGroups = 512;
+// partition; at most max_decode_splits() partitions (the merge keeps one
+// weight per partition in LDS).  One workgroup per CU measured fastest: with
+// S = 1 the second (merge) launch disappears as well.
+static const int32_t kTargetGroups = 256;
 
 extern "C" kvs_status kvs_decode_splits(const kvs_plan* plan, int32_t batch, int32_t max_seq_len,
                                         int32_t* n_splits) {

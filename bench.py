@@ -3,7 +3,10 @@
 A step is one decode step of the whole hot path over all layers of the
 workload: every owner layer appends its new token's K/V (kvs_append, n=1),
 then every layer runs split-K decode attention over its source slot(s)
-(kvs_attn_decode, one launch: partitions + fused merge).  Inputs are
+(kvs_attn_decode: the partition kernel, plus a small merge kernel when the
+sequence is split into several partitions).  The factorized workload
+appends the new token's coefficients, codes, scales and rank
+(kvs_append_factorized) instead of K/V.  Inputs are
 resident in HBM before the timed region; K/V and queries are seeded
 synthetic N(0,1) tensors of the workload's shapes.
 
@@ -74,6 +77,49 @@ def setup(wl):
         del k, v
     torch.cuda.synchronize()
     return src, w, plan, cache, owners
+
+
+def setup_factorized(wl):
+    """Factorized cache: every layer pair's coefficients and bases, every
+    layer's int8 residual codes, scales and directions, per-token ranks."""
+    src, w = datagen.share_map(wl)
+    cfg = K.make_config(wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, "bf16", wl.batch,
+                        wl.ctx, kind=K.KVS_FACTORIZED, basis_rank=wl.basis_rank,
+                        resid_rank_max=wl.resid_rank_max)
+    plan = K.kvs_share_plan(cfg, src, w)
+    cache = K.Cache(plan, "cuda")
+    owners = datagen.owner_layers(src)
+    Hkv, R, Rm, hd = wl.n_kv_heads, wl.basis_rank, wl.resid_rank_max, wl.head_dim
+    rank = datagen.token_ranks(wl, device="cuda")
+    bk_all = cache.basis_k.view(torch.bfloat16).view(len(owners), Hkv, R, hd)
+    bv_all = cache.basis_v.view(torch.bfloat16).view(len(owners), Hkv, R, hd)
+    uk_all = cache.ubasis_k.view(torch.bfloat16).view(wl.n_layers, Hkv, Rm, hd)
+    uv_all = cache.ubasis_v.view(torch.bfloat16).view(wl.n_layers, Hkv, Rm, hd)
+    zeros = torch.zeros(wl.batch, dtype=torch.int32, device="cuda")
+    for l in range(wl.n_layers):
+        ck = cv = None
+        if l in owners:
+            ck, cv = datagen.pair_coeffs(wl, l // 2, device="cuda")
+            bk, bv = datagen.pair_basis(wl, l // 2, device="cuda")
+            bk_all[owners.index(l)].copy_(bk)
+            bv_all[owners.index(l)].copy_(bv)
+        uk, uv = datagen.layer_residual_basis(wl, l, device="cuda")
+        uk_all[l].copy_(uk)
+        uv_all[l].copy_(uv)
+        dk, dv, sk, sv = datagen.layer_residual(wl, l, rank, device="cuda")
+        K.kvs_append_factorized(plan, cache, l, ck, cv, dk, dv, sk, sv,
+                                rank if l == 0 else None, zeros)
+    torch.cuda.synchronize()
+    return src, w, plan, cache, owners, rank
+
+
+def fact_bytes_per_call(wl, rank):
+    """Algorithmic bytes of one factorized decode call: per (sequence, KV head,
+    token) both coefficient rows (2 x 32 bf16), r_t int8 codes for K and for
+    V, two fp16 scales; one rank byte per (sequence, token)."""
+    tokens = wl.batch * wl.ctx
+    sum_r = int(rank.to(torch.int64).sum())
+    return wl.n_kv_heads * (tokens * (2 * wl.basis_rank * 2 + 4) + 2 * sum_r) + tokens
 
 
 def cpu_baseline(wl, src, w, host_seq, budget_s=12.0):
@@ -180,7 +226,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tinyllama_cla2",
-                    choices=["tiny_cla2", "tinyllama_cla2", "depthgraft", "cla2_64k"])
+                    choices=["tiny_cla2", "tinyllama_cla2", "depthgraft", "cla2_64k",
+                             "factorized_64k"])
     ap.add_argument("--roofline-passes", type=int, default=3)
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the cache-flushed per-launch timing loop (for profiling)")
@@ -199,13 +246,36 @@ def main():
     wl = datagen.WORKLOADS[args.workload]
     torch.cuda.set_device(0)
     log(f"[bench] setting up {wl.name}")
-    src, w, plan, cache, owners = setup(wl)
+    fact = wl.kind == "factorized"
+    if fact:
+        src, w, plan, cache, owners, rank = setup_factorized(wl)
+    else:
+        src, w, plan, cache, owners = setup(wl)
     L, B = wl.n_layers, wl.batch
     qs = [datagen.decode_q(wl, l, device="cuda") for l in range(L)]
-    new_kv = {l: datagen.owner_kv(wl, 1000 + l, device="cuda", ctx=1) for l in owners}
     # the step's token lands at position ctx-1 (rewritten every step); the
     # query attends over ctx keys including it
     pos = torch.full((B,), wl.ctx - 1, dtype=torch.int32, device="cuda")
+    if fact:
+        one = wl.with_(ctx=1)
+        r1 = rank[:, wl.ctx - 1:].contiguous()
+        new_f = {}
+        for l in range(L):
+            cc = datagen.pair_coeffs(one, 1000 + l, device="cuda") if l in owners else (None, None)
+            new_f[l] = cc + datagen.layer_residual(one, 1000 + l, r1, device="cuda")
+
+        def append(l):
+            ck, cv, dk, dv, sk, sv = new_f[l]
+            K.kvs_append_factorized(plan, cache, l, ck, cv, dk, dv, sk, sv,
+                                    r1 if l == 0 else None, pos, stream=stream)
+        call_bytes = [fact_bytes_per_call(wl, rank)] * L
+    else:
+        new_kv = {l: datagen.owner_kv(wl, 1000 + l, device="cuda", ctx=1) for l in owners}
+
+        def append(l):
+            if l in new_kv:
+                K.kvs_append(plan, cache, l, new_kv[l][0], new_kv[l][1], pos, stream=stream)
+        call_bytes = [bytes_per_call(wl, src, l) for l in range(L)]
     seq_len = torch.full((B,), wl.ctx, dtype=torch.int32, device="cuda")
     n_splits = K.kvs_decode_splits(plan, B, wl.ctx)
     ws = torch.zeros(K.kvs_decode_workspace_size(plan, B, n_splits), dtype=torch.uint8,
@@ -220,8 +290,7 @@ def main():
 
     def step():
         for l in range(L):
-            if l in new_kv:
-                K.kvs_append(plan, cache, l, new_kv[l][0], new_kv[l][1], pos, stream=stream)
+            append(l)
             decode(l)
 
     res = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -241,7 +310,7 @@ def main():
         t1.record(stream)
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / args.steps
-        step_bytes = sum(bytes_per_call(wl, src, l) for l in range(L))
+        step_bytes = sum(call_bytes)
         res |= {"value": B * 1000.0 / ms, "ms_per_step": ms,
                 "step_hbm_gbs": step_bytes / (ms * 1e-3) / 1e9,
                 "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
@@ -271,23 +340,25 @@ def main():
 
     dom = single if single else mixed
     us = avg_us(dom)
-    nbytes = bytes_per_call(wl, src, dom[0])
+    nbytes = call_bytes[dom[0]]
     achieved = nbytes / (us * 1e-6) / 1e9
     res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                       "kernel": "decode_kernel (split-K partitions + fused merge), "
-                                 + ("single-source layer" if single else "two-source layer"),
+                       "kernel": ("fact_decode_kernel (factorized cache, split-K partitions)"
+                                  if fact else
+                                  "decode_kernel (split-K partitions), "
+                                  + ("single-source layer" if single else "two-source layer")),
                        "bytes_per_launch": nbytes, "avg_launch_us": us,
                        "launches": sum(len(timed[l]) for l in dom), "cache": "flushed"}
     if single and mixed:
         us2 = avg_us(mixed)
-        b2 = bytes_per_call(wl, src, mixed[0])
+        b2 = call_bytes[mixed[0]]
         res["roofline_two_source"] = {"achieved": b2 / (us2 * 1e-6) / 1e9,
                                       "frac": b2 / (us2 * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                       "bytes_per_launch": b2, "avg_launch_us": us2}
     del flush
 
-    if not args.roofline_only and not args.no_cpu_baseline:
+    if not args.roofline_only and not args.no_cpu_baseline and not fact:
         log("[bench] cpu baseline")
         full = {}
         for l in owners:

@@ -107,9 +107,9 @@ typedef struct {
 
 /* Byte sizes of the caller-allocated device buffers.  Pool layouts (64-token
  * pages; page p of sequence b lives in physical page page_table[b][p]):
- *   dense K pool  [n_slots][n_phys_pages][Hkv][4][hd/(4E)][16][4][E],
+ *   dense K pool  [n_slots][n_phys_pages][Hkv][8][hd/(8E)][8][8][E],
  *                 E = 16 B / elem: chunk c (E elements) of token t of a page
- *                 at (((t/16)*(hd/(4E)) + c/4)*64 + 4*(t%16) + c%4)*E
+ *                 at (((t/8)*(hd/(8E)) + c/8)*64 + 8*(t%8) + c%8)*E
  *   dense V pool  [n_slots][n_phys_pages][Hkv][32][hd][2]     token pairs
  *                 (element (t, d) of a page at (t/2)*hd*2 + d*2 + t%2)
  *   page table    [max_batch][pages_per_seq] int32 in [0, n_phys_pages)

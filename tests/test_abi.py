@@ -129,8 +129,8 @@ def test_decode_split_choice_and_workspace():
     src, w = datagen.share_map(wl)
     plan = K.kvs_share_plan(_cfg(32, 32, 8, 128, "bf16", 4, 65536), src, w)
     s = K.kvs_decode_splits(plan, 4, 65536)
-    # one 4-wave workgroup per (partition, KV head, sequence): about 512 of them
-    assert 1 <= s <= 64 and 4 * 8 * s >= 512
+    # one 4-wave workgroup per (partition, KV head, sequence): about 256 of them
+    assert 1 <= s <= 64 and 4 * 8 * s >= 256
     assert K.kvs_decode_splits(plan, 4, 64) == 1
     # partials [B][Hq][S][hd], maxima and sums [B][Hq][S]
     assert K.kvs_decode_workspace_size(plan, 4, s) == 4 * 32 * s * (128 + 2) * 4

@@ -138,11 +138,11 @@ def test_append_layout_bit_exact_and_incremental():
             for kvh in range(Hkv):
                 base = _page_offset(pt, b, pos, kvh, hd, Hkv, n_phys, 0)
                 t = pos % 64
-                E, ncq = 8, hd // 32
+                E, ncw = 8, hd // 64
 
                 def koff(d):
                     c = d // E
-                    return (((t // 16) * ncq + c // 4) * 64 + 4 * (t % 16) + c % 4) * E + d % E
+                    return (((t // 8) * ncw + c // 8) * 64 + 8 * (t % 8) + c % 8) * E + d % E
 
                 krow = torch.stack([kp[base + koff(d)] for d in range(hd)])
                 vrow = torch.stack([vp[base + (t // 2) * hd * 2 + d * 2 + t % 2] for d in range(hd)])
