@@ -146,6 +146,140 @@ def cpu_baseline(wl, src, w, host_seq, budget_s=12.0):
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+CALIB_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {"decode_kernel": "k_decode.hip", "fact_decode_kernel": "k_factorized.hip",
+                  "prefill_kernel": "k_prefill.hip"}
+
+
+def source_digest(kernel):
+    import hashlib
+    path = os.path.join(ROOT, "attention_cross_layer_amd", "csrc",
+                        KERNEL_SOURCES[kernel.split("<")[0]])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch measured by the committed counter profile of this
+    workload's dominant kernel, or None when there is none or the kernel's
+    source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = json.load(open(TRAFFIC_FILE)).get(workload)
+    if not rec or rec["source_sha256_16"] != source_digest(rec["kernel"]):
+        return None
+    return {"bytes_per_launch": rec["fetch_bytes"] + rec["write_bytes"],
+            "source": f"rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated ({rec['profile']})"}
+
+
+def summarize(prof_dir, kernel, workload):
+    """Summarise a profile directory holding kt/ (--kernel-trace --stats),
+    fetch/ (--pmc FETCH_SIZE) and write/ (--pmc WRITE_SIZE) runs of
+    ``bench.py --roofline-only``: average duration of ``kernel`` and its
+    counter bytes per dispatch, scaled by what the same counters read for the
+    run's 256 MiB reference copy."""
+    import csv
+    import glob
+
+    def rows(sub, name):
+        f = glob.glob(os.path.join(prof_dir, sub, "*" + name))
+        return list(csv.DictReader(open(f[0]))) if f else []
+
+    # ``kernel`` is a kernel name (every instantiation) or one instantiation,
+    # e.g. "decode_kernel<unsigned short, 128, 4, 1>"
+    key = "::" + kernel + ("" if "<" in kernel else "<")
+
+    def match(name):
+        return key in name
+
+    stats = [r for r in rows("kt", "kernel_stats.csv") if match(r["Name"])]
+    out = {"kernel": kernel, "workload": workload}
+    if stats:
+        calls = sum(int(r["Calls"]) for r in stats)
+        tot = sum(float(r["TotalDurationNs"]) for r in stats)
+        out |= {"calls": calls, "avg_us": tot / calls / 1e3}
+    for sub, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        rs = [r for r in rows(sub, "counter_collection.csv") if r["Counter_Name"] == counter]
+        mine = [float(r["Counter_Value"]) for r in rs if match(r["Kernel_Name"])]
+        # the reference copy is the run's last device-to-device copy dispatch
+        copy = [float(r["Counter_Value"]) for r in rs if "copyBuffer" in r["Kernel_Name"]]
+        if mine and copy:
+            scale = CALIB_BYTES / (copy[-1] * 1024)      # bytes per counted byte
+            out[counter] = {"kib_per_dispatch": sum(mine) / len(mine),
+                            "copy_kib": copy[-1], "scale": scale,
+                            "bytes_per_dispatch": sum(mine) / len(mine) * 1024 * scale}
+    return out
+
+
+def algorithmic_bytes(wl, kernel):
+    """Algorithmic bytes of one launch of the profiled kernel: a dense decode
+    launch of a layer with as many sources as the instantiation's last
+    template argument (one when the name carries none), or a factorized
+    decode launch."""
+    if kernel.startswith("fact_decode_kernel"):
+        B, T = wl.batch, wl.ctx
+        n_hi = int(round(wl.rank16_frac * T))
+        sum_r = B * (16 * n_hi + 8 * ((T - n_hi) // 2))   # exact per-rank token counts
+        tokens = B * T
+        return wl.n_kv_heads * (tokens * (2 * wl.basis_rank * 2 + 4) + 2 * sum_r) + tokens
+    nsrc = int(kernel.rstrip(">").split(",")[-1]) if "<" in kernel else 1
+    elem = 4 if wl.dtype == "f32" else 2
+    return wl.batch * wl.n_kv_heads * wl.ctx * wl.head_dim * 2 * elem * nsrc
+
+
+def record_profile(prof_dir, kernel, workload, s):
+    """Write profiles/<kernel>_<workload>.md from a summarised profile
+    directory and store its counter bytes in profiles/traffic.json."""
+    import csv
+    import glob
+
+    wl = datagen.WORKLOADS[workload]
+    base = kernel.split("<")[0]
+    f = glob.glob(os.path.join(prof_dir, "kt", "*kernel_stats.csv"))
+    allk = sorted(csv.DictReader(open(f[0])), key=lambda r: -float(r["TotalDurationNs"]))
+    top = [r for r in allk if "kvs::" in r["Name"]] + [r for r in allk if "kvs::" not in r["Name"]][:4]
+    alg = algorithmic_bytes(wl, kernel)
+    fetch, write = s["FETCH_SIZE"]["bytes_per_dispatch"], s["WRITE_SIZE"]["bytes_per_dispatch"]
+    cmd = f"python3 bench.py --workload {workload} --roofline-only"
+    lines = [
+        f"# `{kernel}` on `{workload}`", "",
+        "Commands (from the repository root, profile directory `P`):", "", "```",
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d P/kt -o run -- {cmd}",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d P/fetch -o run -- {cmd}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d P/write -o run -- {cmd}",
+        f"python3 bench.py --summarize P --kernel '{kernel}' --workload {workload} --record",
+        "```", "",
+        f"Kernel source sha256[:16]: `{s['source_sha256_16']}`", "",
+        f"## `{kernel}`", "",
+        f"- dispatches: {s['calls']}, average duration {s['avg_us']:.2f} us",
+        f"- algorithmic bytes per launch: {alg:,}",
+        f"- FETCH_SIZE: {s['FETCH_SIZE']['kib_per_dispatch']:.1f} KiB/dispatch x "
+        f"{s['FETCH_SIZE']['scale']:.4f} (copy calibration: 256 MiB read counted as "
+        f"{s['FETCH_SIZE']['copy_kib']:.1f} KiB) = {fetch:,.0f} B "
+        f"({fetch / alg:.3f} x algorithmic)",
+        f"- WRITE_SIZE: {s['WRITE_SIZE']['kib_per_dispatch']:.1f} KiB/dispatch x "
+        f"{s['WRITE_SIZE']['scale']:.4f} = {write:,.0f} B",
+        f"- algorithmic rate at the traced average: {alg / (s['avg_us'] * 1e-6) / 1e9:,.0f} GB/s "
+        f"({alg / (s['avg_us'] * 1e-6) / 1e9 / HBM_PEAK_GBS:.1%} of 8 TB/s)", "",
+        "## Kernels of the traced run: this library's, then the largest others (set-up, "
+        "and the 512 MB read that flushes the cache before each timed launch)", "",
+        "| kernel | calls | avg us | share |", "|---|---:|---:|---:|"]
+    for r in top:
+        name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0]
+        name = name.replace("void ", "").replace("|", "/")
+        if len(name) > 90:
+            name = name[:87] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f}% |")
+    out = os.path.join(ROOT, "profiles", f"{base}_{workload}.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    rec = json.load(open(TRAFFIC_FILE)) if os.path.exists(TRAFFIC_FILE) else {}
+    rec[workload] = {"kernel": kernel, "source_sha256_16": s["source_sha256_16"],
+                     "fetch_bytes": round(fetch), "write_bytes": round(write),
+                     "algorithmic_bytes": alg, "avg_us": s["avg_us"],
+                     "profile": os.path.relpath(out, ROOT)}
+    json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
+    return out
 
 
 def prefill_flops(n, T, n_q_heads, hd):
@@ -232,9 +366,24 @@ def main():
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the cache-flushed per-launch timing loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize", metavar="PROFILE_DIR",
+                    help="print the counter summary of a rocprofv3 profile directory and exit")
+    ap.add_argument("--kernel", default="decode_kernel",
+                    help="kernel name, or one instantiation such as "
+                         "'decode_kernel<unsigned short, 128, 4, 1>'")
+    ap.add_argument("--record", action="store_true",
+                    help="with --summarize: write profiles/<kernel>_<workload>.md and "
+                         "the workload's entry of profiles/traffic.json")
     ap.add_argument("--prefill", action="store_true",
                     help="time the DepthGraft causal prefill chunk instead of decode")
     args = ap.parse_args()
+    if args.summarize:
+        s = summarize(args.summarize, args.kernel, args.workload)
+        s["source_sha256_16"] = source_digest(args.kernel)
+        print(json.dumps(s, indent=1))
+        if args.record:
+            print(record_profile(args.summarize, args.kernel, args.workload, s))
+        return
     if args.prefill:
         return prefill_main(args)
     if args.gpus != 1:
@@ -356,7 +505,19 @@ def main():
         res["roofline_two_source"] = {"achieved": b2 / (us2 * 1e-6) / 1e9,
                                       "frac": b2 / (us2 * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                       "bytes_per_launch": b2, "avg_launch_us": us2}
-    del flush
+    # ---- reference copy of known size for calibrating the HBM byte
+    # counters of a profiled run: 256 MiB read + 256 MiB written by
+    # PyTorch's elementwise copy kernel, cache flushed first
+    ref_src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    ref_dst = torch.empty_like(ref_src)
+    flush.sum(dim=0)
+    ref_dst.copy_(ref_src)
+    torch.cuda.synchronize()
+    del flush, ref_src, ref_dst
+    traffic = recorded_traffic(wl.name)
+    if traffic is not None:
+        res["roofline"]["traffic"] = traffic["bytes_per_launch"]
+        res["roofline"]["traffic_source"] = traffic["source"]
 
     if not args.roofline_only and not args.no_cpu_baseline and not fact:
         log("[bench] cpu baseline")
