@@ -411,51 +411,41 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
 
 // Merge of the S partitions of one (sequence, KV head): for each of its G
 // query heads, out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with
-// M = max_s m_s, summed in partition order (deterministic).  Partitions with
-// no pages were never written and are skipped.  grid (Hkv, B), 256 threads;
-// all loads of a thread are independent, so they overlap.
+// M = max_s m_s, summed in partition order (deterministic).  Every partition
+// writes its row, an empty one as (O = 0, m = -inf, l = 0), so no partition
+// is skipped and no load waits on another: the maxima and sums go to LDS in
+// one parallel pass, then each thread's S partial loads are independent.
+// grid (Hkv, B), 256 threads.
 template <int G, int HD>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams a) {
-  __shared__ float f_lds[G * kMaxFusedSplits];
-  __shared__ float den_lds[G];
+  __shared__ float m_lds[G * kMaxFusedSplits];
+  __shared__ float l_lds[G * kMaxFusedSplits];
   const int tid = threadIdx.x;
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int S = a.n_splits;
-  const int n_keys = clamp_len(a.seq_len[b], a.max_ctx);
-  const int n_pages = (n_keys + kPage - 1) / kPage;
   const size_t hq0 = (size_t)b * a.n_q_heads + (size_t)kvh * G;
+  // rows (hq0 + h) * S + s of the G heads are contiguous
   for (int i = tid; i < G * S; i += 256) {
-    const int h = i / S, s = i % S;
-    int qb, qe;
-    split_range(n_pages, s, S, qb, qe);
-    f_lds[i] = qb < qe ? a.ws_m[(hq0 + h) * S + s] : -INFINITY;
-  }
-  __syncthreads();
-  if (tid < G) {
-    const int h = tid;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, f_lds[h * S + s]);
-    float den = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float ms = f_lds[h * S + s];
-      const float f = (ms == -INFINITY) ? 0.f : dev::fast_exp2(ms - M);
-      if (f != 0.f) den = fmaf(f, a.ws_l[(hq0 + h) * S + s], den);
-      f_lds[h * S + s] = f;
-    }
-    den_lds[h] = den;
+    m_lds[i] = a.ws_m[hq0 * S + i];
+    l_lds[i] = a.ws_l[hq0 * S + i];
   }
   __syncthreads();
   for (int e = tid; e < G * HD; e += 256) {
     const int h = e / HD, d = e % HD;
+    const float* ml = m_lds + h * S;
+    const float* ll = l_lds + h * S;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s]);
     const float* o = a.ws_o + (hq0 + h) * S * HD + d;
-    float num = 0.f;
+    float num = 0.f, den = 0.f;
+    if (M != -INFINITY) {
 #pragma unroll 8
-    for (int s = 0; s < S; ++s) {
-      const float f = f_lds[h * S + s];
-      const float x = o[(size_t)s * HD];
-      num = (f != 0.f) ? fmaf(f, x, num) : num;   // unwritten partitions hold stale bytes
+      for (int s = 0; s < S; ++s) {
+        const float f = dev::fast_exp2(ml[s] - M);   // 0 for an empty partition
+        num = fmaf(f, o[(size_t)s * HD], num);
+        den = fmaf(f, ll[s], den);
+      }
     }
-    const float den = den_lds[h];
     store_out(a.out, (hq0 + h) * HD + d, den > 0.f ? num / den : 0.f, a.out_bf16);
   }
 }

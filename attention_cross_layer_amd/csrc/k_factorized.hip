@@ -359,52 +359,62 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
 }
 
 // Merge of S partitions in coefficient space, then the basis projection.
+// Every partition writes its row (an empty one as c = 0, m = -inf, l = 0).
+// Loads that do not depend on each other are issued together: the maxima and
+// sums to LDS, each thread's basis column (its d is fixed: 256 is a multiple
+// of HD) into registers, then the S coefficient partials.
 template <int HD, int G>
 __global__ __launch_bounds__(256) void fact_merge_kernel(FactParams a) {
-  __shared__ float f_lds[G * kMaxSplitsF];
+  static_assert(256 % HD == 0, "a thread keeps one output column");
+  __shared__ float m_lds[G * kMaxSplitsF];
+  __shared__ float l_lds[G * kMaxSplitsF];
   __shared__ float den[G];
   __shared__ float coef[G * kW];
   const int tid = threadIdx.x;
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int S = a.n_splits;
-  const int n_keys = min(max(a.seq_len[b], 0), a.max_ctx);
-  const int n_pages = (n_keys + kPage - 1) / kPage;
   const size_t hq0 = (size_t)b * a.n_q_heads + (size_t)kvh * G;
   for (int i = tid; i < G * S; i += 256) {
-    const int h = i / S, s = i % S;
-    int qb, qe;
-    split_range(n_pages, s, S, qb, qe);
-    f_lds[i] = qb < qe ? a.ws_m[(hq0 + h) * S + s] : -INFINITY;
+    m_lds[i] = a.ws_m[hq0 * S + i];
+    l_lds[i] = a.ws_l[hq0 * S + i];
   }
-  __syncthreads();
-  if (tid < G) {
-    const int h = tid;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, f_lds[h * S + s]);
-    float dsum = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float ms = f_lds[h * S + s];
-      const float f = (ms == -INFINITY) ? 0.f : dev::fast_exp2(ms - M);
-      if (f != 0.f) dsum = fmaf(f, a.ws_l[(hq0 + h) * S + s], dsum);
-      f_lds[h * S + s] = f;
-    }
-    den[h] = dsum;
+  const int d = tid % HD;
+  float col[kW];   // column d of B^V (rows 0..R-1) then U^V (rows R..R+RM-1)
+  {
+    const uint16_t* bv = a.bv + (size_t)kvh * kR * HD + d;
+    const uint16_t* uv = a.uv + (size_t)kvh * kRM * HD + d;
+#pragma unroll
+    for (int i = 0; i < kR; ++i) col[i] = __uint_as_float((uint32_t)bv[i * HD] << 16);
+#pragma unroll
+    for (int j = 0; j < kRM; ++j) col[kR + j] = __uint_as_float((uint32_t)uv[j * HD] << 16);
   }
   __syncthreads();
   for (int e = tid; e < G * kW; e += 256) {
     const int h = e / kW, i = e % kW;
+    const float* ml = m_lds + h * S;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s]);
     const float* c = a.ws_c + (hq0 + h) * S * kW + i;
-    float acc = 0.f;
+    float acc = 0.f, l = 0.f;
+    if (M != -INFINITY) {
 #pragma unroll 8
-    for (int s = 0; s < S; ++s) {
-      const float f = f_lds[h * S + s];
-      const float x = c[(size_t)s * kW];
-      acc = (f != 0.f) ? fmaf(f, x, acc) : acc;
+      for (int s = 0; s < S; ++s) {
+        const float f = dev::fast_exp2(ml[s] - M);   // 0 for an empty partition
+        acc = fmaf(f, c[(size_t)s * kW], acc);
+        l = fmaf(f, l_lds[h * S + s], l);
+      }
     }
     coef[e] = acc;
+    if (i == 0) den[h] = l;
   }
   __syncthreads();
-  project_out<HD, G>(a, b, kvh, coef, den, tid, 256);
+  for (int h = tid / HD; h < G; h += 256 / HD) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < kW; ++i) acc = fmaf(coef[h * kW + i], col[i], acc);
+    const float l = den[h];
+    store_out(a.out, (hq0 + h) * HD + d, l > 0.f ? acc / l : 0.f, a.out_bf16);
+  }
 }
 
 template <int HD, int G>
