@@ -101,7 +101,8 @@ extern "C" kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cac
       return fail(KVS_ERR_ARG, "null factorized cache buffer");
     if (!aligned16(cache->ck_pool) || !aligned16(cache->cv_pool) || !aligned16(cache->dk_pool) ||
         !aligned16(cache->dv_pool) || !aligned16(cache->basis_k) || !aligned16(cache->basis_v) ||
-        !aligned16(cache->ubasis_k) || !aligned16(cache->ubasis_v) || !aligned4(cache->page_table))
+        !aligned16(cache->ubasis_k) || !aligned16(cache->ubasis_v) || !aligned16(cache->sk_pool) ||
+        !aligned16(cache->sv_pool) || !aligned16(cache->rank_pool) || !aligned4(cache->page_table))
       return fail(KVS_ERR_ALIGN, "factorized buffers must be 16-byte aligned");
     FactDecodeLaunch f;
     f.ck_pool = cache->ck_pool;
@@ -227,7 +228,7 @@ extern "C" kvs_status kvs_append_factorized(const kvs_plan* plan, const kvs_cach
   if (st != KVS_OK) return st;
   const Plan& p = plan->p;
   if (p.cfg.kind != KVS_FACTORIZED) return fail(KVS_ERR_ARG, "kvs_append_factorized needs a factorized plan");
-  if (!cache || !dk || !dv || !sk || !sv || !start_pos) return fail(KVS_ERR_ARG, "null argument");
+  if (!cache || !dk || !dv || !sk || !sv || !rank || !start_pos) return fail(KVS_ERR_ARG, "null argument");
   if (!cache->ck_pool || !cache->cv_pool || !cache->dk_pool || !cache->dv_pool || !cache->sk_pool ||
       !cache->sv_pool || !cache->rank_pool || !cache->page_table)
     return fail(KVS_ERR_ARG, "null cache pool");
@@ -241,7 +242,8 @@ extern "C" kvs_status kvs_append_factorized(const kvs_plan* plan, const kvs_cach
       !aligned16(cache->ck_pool) || !aligned16(cache->cv_pool) || !aligned16(cache->dk_pool) ||
       !aligned16(cache->dv_pool))
     return fail(KVS_ERR_ALIGN, "coefficients, codes and pools must be 16-byte aligned");
-  if (!aligned4(start_pos) || !aligned4(cache->page_table) || ((uintptr_t)sk & 1) || ((uintptr_t)sv & 1))
+  if (!aligned4(start_pos) || !aligned4(cache->page_table) || ((uintptr_t)sk & 1) || ((uintptr_t)sv & 1) ||
+      ((uintptr_t)cache->rank_pool & 1))
     return fail(KVS_ERR_ALIGN, "misaligned scale or int32 array");
   if (n == 0) return KVS_OK;
   FactAppendLaunch a;

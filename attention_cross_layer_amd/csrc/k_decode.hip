@@ -411,39 +411,46 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
 
 // Merge of the S partitions of one (sequence, KV head): for each of its G
 // query heads, out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with
-// M = max_s m_s, summed in partition order (deterministic).  Every partition
-// writes its row, an empty one as (O = 0, m = -inf, l = 0), so no partition
-// is skipped and no load waits on another: the maxima and sums go to LDS in
-// one parallel pass, then each thread's S partial loads are independent.
+// M = max_s m_s.  Every partition writes its row, an empty one as
+// (O = 0, m = -inf, l = 0), so a thread loads its S (m, l, O) triples 16 at
+// a time with no dependence between them and folds each batch into a running
+// (M, num, den); the order is fixed, so the result is deterministic.
 // grid (Hkv, B), 256 threads.
 template <int G, int HD>
 __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams a) {
-  __shared__ float m_lds[G * kMaxFusedSplits];
-  __shared__ float l_lds[G * kMaxFusedSplits];
   const int tid = threadIdx.x;
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int S = a.n_splits;
   const size_t hq0 = (size_t)b * a.n_q_heads + (size_t)kvh * G;
-  // rows (hq0 + h) * S + s of the G heads are contiguous
-  for (int i = tid; i < G * S; i += 256) {
-    m_lds[i] = a.ws_m[hq0 * S + i];
-    l_lds[i] = a.ws_l[hq0 * S + i];
-  }
-  __syncthreads();
   for (int e = tid; e < G * HD; e += 256) {
     const int h = e / HD, d = e % HD;
-    const float* ml = m_lds + h * S;
-    const float* ll = l_lds + h * S;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s]);
-    const float* o = a.ws_o + (hq0 + h) * S * HD + d;
-    float num = 0.f, den = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll 8
-      for (int s = 0; s < S; ++s) {
-        const float f = dev::fast_exp2(ml[s] - M);   // 0 for an empty partition
-        num = fmaf(f, o[(size_t)s * HD], num);
-        den = fmaf(f, ll[s], den);
+    const float* mrow = a.ws_m + (hq0 + h) * S;
+    const float* lrow = a.ws_l + (hq0 + h) * S;
+    const float* orow = a.ws_o + (hq0 + h) * S * HD + d;
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 16) {
+      float mv[16], lv[16], ov[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int s = min(s0 + k, S - 1);
+        mv[k] = s0 + k < S ? mrow[s] : -INFINITY;
+        lv[k] = lrow[s];
+        ov[k] = orow[(size_t)s * HD];
+      }
+      float Mn = M;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) Mn = fmaxf(Mn, mv[k]);
+      if (Mn != -INFINITY) {
+        const float r = dev::fast_exp2(M - Mn);   // 0 while M is -inf
+        num *= r;
+        den *= r;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float f = dev::fast_exp2(mv[k] - Mn);   // 0 for empty or absent partitions
+          num = fmaf(f, ov[k], num);
+          den = fmaf(f, lv[k], den);
+        }
+        M = Mn;
       }
     }
     store_out(a.out, (hq0 + h) * HD + d, den > 0.f ? num / den : 0.f, a.out_bf16);

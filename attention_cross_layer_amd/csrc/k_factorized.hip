@@ -13,26 +13,36 @@
 // Decode.  The attention of one query row over these keys/values is
 //   z_t = q . K_t = c_t . (B q) + s_t * sum_{j<r_t} d_{t,j} (U_j . q)
 //   out = sum_t p_t V_t = (sum_t p_t c^V_t) B^V + (sum_t p_t s^V_t d^V_t) U^V,
-// the same values the explicit rebuild gives (up to rounding order).  The
-// kernel therefore contracts the bases with the query once per workgroup
-// (q~ = B^K q, u~ = U^K q), streams the coefficients, codes, scales and ranks
-// once per (sequence, KV head) for all G query heads, accumulates in the
-// 48-wide coefficient space, and applies B^V / U^V once per output row.
-// Per token it moves 64+64 B of coefficients, 16+16 B of codes, 4 B of scales
-// and the rank byte, and spends about 0.6 KFLOP instead of the 24.6 KFLOP an
-// explicit 64x128 tile rebuild would cost.
+// the same values the explicit rebuild gives (up to rounding order).  A
+// workgroup contracts the bases with its G queries once (q~ = B^K q,
+// u~ = U^K q), streams each page's coefficients, codes and scales once for
+// all G query heads, and accumulates in the 48-wide coefficient space;
+// B^V / U^V are applied once per output row.  Per page of 64 tokens the two
+// contractions are small dense products, [64 x 48] x [48 x G] for the scores
+// and [G x 64] x [64 x 48] for the values.  Both run on the 4x4x4 bf16 MFMA
+// (16 independent 4x4 blocks per instruction: a wave's lanes are 16 token
+// quads x 4 heads), which keeps the whole chain in registers:
+//   scores   A = coefficients or codes (lane = token, 4 per block),
+//            B = q~ as a bf16 high part plus the bf16 rounding of the rest
+//            (two products into one accumulator, exact to about 2^-17),
+//            D = lane (quad q, head p): tokens 4q..4q+3 of head p;
+//   values   A = those probabilities, straight from the score registers,
+//            B = value coefficients / codes (lane (quad q, column j):
+//            tokens 4q..4q+3), D accumulated per quad; the 16 quads are
+//            summed once at the end.
 //
 // Page layouts (64 tokens per page and KV head):
-//   cK  [4][64][8] bf16     coefficient chunk cc (8 values) of token t at
-//                            (cc*64 + t)*8: a 1 KiB contiguous load per chunk
-//   cV  [32][32][2] bf16    token pairs: (t, i) at (t/2)*64 + i*2 + t%2
-//   dK  [64][16] int8        16 codes of token t at t*16
-//   dV  [32][16][2] int8     token pairs: (t, j) at (t/2)*32 + j*2 + t%2
-//   sK, sV [64] fp16; rank [64] uint8 per physical page (shared by all heads
-//   and layers)
-// Decomposition: grid (S, Hkv, B) of 4-wave workgroups, split-K over pages
-// as in the dense decode, with the same LDS merge of the 4 waves and the
-// same second-kernel merge across partitions (in coefficient space).
+//   cK  [4][64][8] bf16      coefficients 8cc..8cc+7 of token t at (cc*64 + t)*8
+//   cV  [4][64][2][4] bf16   coefficient i of token t (m = i/4, lane = 4*(t/4) + i%4)
+//                            at ((m/2)*64 + lane)*8 + (m%2)*4 + t%4
+//   dK, dV  [128][8] int8    rank-packed: token t owns ceil(r_t/8) 8-byte granules
+//                            from granule o_t = sum_{u<t} ceil(r_u/8); its codes
+//                            j >= r_t inside them are zero
+//   sK, sV  [64] fp16
+//   meta    [64] uint16 per physical page, shared by all layers and heads:
+//           r_t | o_t << 8
+// so a decode reads ceil(r_t/8)*8 code bytes per token (exactly r_t for
+// ranks that are multiples of 8), not a fixed 16.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -46,16 +56,22 @@ namespace {
 
 using dev::dot2_bf16;
 
-constexpr int kR = 32;      // basis rank (coefficients per token)
-constexpr int kRM = 16;     // residual codes per token
+constexpr int kR = 32;             // basis rank (coefficients per token)
+constexpr int kRM = 16;            // residual codes per token at most
 constexpr int kW = kR + kRM;
+constexpr int kGranules = 128;     // 8-byte code granules per page blob
 constexpr int kMaxSplitsF = 64;
+
+typedef __attribute__((ext_vector_type(4))) short s4_t;
+typedef __attribute__((ext_vector_type(4))) float f4_t;
+typedef __attribute__((ext_vector_type(2))) uint32_t u2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf2_t;
 
 struct FactParams {
   const uint16_t* ck; const uint16_t* cv;
   const int8_t* dk; const int8_t* dv;
   const uint16_t* sk; const uint16_t* sv;
-  const uint8_t* rank;
+  const uint16_t* meta;
   const uint16_t* bk; const uint16_t* bv;   // basis of the pair's slot: [Hkv][R][hd]
   const uint16_t* uk; const uint16_t* uv;   // residual directions of the layer: [Hkv][RM][hd]
   const int32_t* page_table;
@@ -64,7 +80,7 @@ struct FactParams {
   int32_t n_kv_heads;
   int32_t n_q_heads;
   int64_t coef_off;     // elements to the slot's cK/cV pages
-  int64_t resid_off;    // elements to the layer's dK/dV pages
+  int64_t resid_off;    // bytes to the layer's dK/dV pages
   int64_t scale_off;    // elements to the layer's sK/sV pages
   const uint16_t* q;
   const int32_t* seq_len;
@@ -87,15 +103,88 @@ __device__ __forceinline__ float half_to_float(uint16_t h) {
   return __half2float(__ushort_as_half(h));
 }
 
-// int8 code -> bf16 bits (exact: |d| <= 128 needs at most 8 significant bits)
-__device__ __forceinline__ uint32_t i8_to_bf16(int v) { return __float_as_uint((float)v) >> 16; }
-
 __device__ __forceinline__ void store_out(void* out, size_t idx, float v, int bf16) {
   if (bf16)
     reinterpret_cast<uint16_t*>(out)[idx] = (uint16_t)dev::f32_to_bf16_bits(v);
   else
     reinterpret_cast<float*>(out)[idx] = v;
 }
+
+__device__ __forceinline__ f4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f4_t c) {
+  const u2_t a = {a0, a1}, b = {b0, b1};
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s4_t, a),
+                                                __builtin_bit_cast(s4_t, b), c, 0, 0, 0);
+}
+
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// four int8 codes (the bytes of w) -> four bf16 values (exact: |d| <= 128)
+__device__ __forceinline__ void codes_to_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = pack_bf16((float)(int8_t)(w & 0xffu), (float)(int8_t)((w >> 8) & 0xffu));
+  hi = pack_bf16((float)(int8_t)((w >> 16) & 0xffu), (float)(int8_t)(w >> 24));
+}
+
+// Byte transpose inside a quad of lanes: lane p of the quad holds bytes
+// b[p][0..3]; returns (b[0][p], b[1][p], b[2][p], b[3][p]).  Two exchange
+// steps (16-bit halves with lane p^2, then bytes with lane p^1), each a DPP
+// quad permutation and a byte permute; sel1 / sel2 are the lane's selectors.
+__device__ __forceinline__ uint32_t quad_transpose(uint32_t x, uint32_t sel1, uint32_t sel2) {
+  const uint32_t z = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xf, 0xf, true);
+  const uint32_t w = __builtin_amdgcn_perm(z, x, sel1);
+  const uint32_t z2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)w, 0xB1, 0xf, 0xf, true);
+  return __builtin_amdgcn_perm(z2, w, sel2);
+}
+
+// Max over the 16 quads of a wave for each lane position p (the lanes l with
+// l % 4 == p), returned to every such lane.
+__device__ __forceinline__ float quad_column_max(float x) {
+  x = fmaxf(x, dev::dpp<0x124>(x));   // row_ror:4
+  x = fmaxf(x, dev::dpp<0x128>(x));   // row_ror:8: every lane holds its row's max
+  // across the two halves, then across row pairs (v_permlane32_swap /
+  // v_permlane16_swap with both operands x: the two results hold the two
+  // partners' values)
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Sum over the 4 quads of each 16-lane row for each lane position p: lane
+// 16*row + p (p < 4) then holds the row's sum.
+__device__ __forceinline__ float quad_row_sum(float x) {
+  x += dev::dpp<0x124>(x);
+  x += dev::dpp<0x128>(x);
+  return x;
+}
+
+constexpr uint32_t kOOB = 0x80000000u;   // offset past every resource's end
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u4_t;
+  const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return make_uint2(v.x, v.y);
+}
+
+// One page as loaded: cK, codes and meta with lane = token; cV with lane =
+// (quad, coefficient); the scales with lane = quad.
+struct PageRegs {
+  uint4 ck[4];
+  uint4 cv[4];
+  uint2 dk[2];
+  uint2 dv[2];
+  uint2 sk, sv;
+};
 
 // out[h][d] = (C[h] . B^V[:, d] + D[h] . U^V[:, d]) / l[h] for the G heads of
 // one (sequence, KV head); coef holds [G][48] (C then D), den [G].
@@ -119,237 +208,332 @@ __device__ void project_out(const FactParams& a, int b, int kvh, const float* co
   }
 }
 
+// grid (S, Hkv, B), 4 waves; wave w walks pages pb+w, pb+w+4, ... of its
+// partition, with the next page's loads in flight while it computes one.
 template <int HD, int G>
 __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
-  __shared__ float qt[G][kW];                  // (B^K q, U^K q) * log2(e)/sqrt(hd)
-  __shared__ uint32_t p_lds[4][32 * G];        // p of a key pair, packed bf16
-  __shared__ uint32_t ps_lds[4][32 * G];       // p * s^V of a key pair, packed bf16
-  __shared__ float mrg_c[4][G][kW];
-  __shared__ float mrg_m[4][G];
-  __shared__ float mrg_l[4][G];
+  constexpr int NB = (G + 3) / 4;              // blocks of 4 query heads
+  __shared__ float qt[NB * 4][kW];             // (B^K q, U^K q) * log2(e)/sqrt(hd)
+  __shared__ float part[4][4][NB * 4][kW];     // [wave][16-lane row][head][coefficient]
+  __shared__ float part_l[4][4][NB * 4];
+  __shared__ float wave_m[4][NB * 4];
   __shared__ float fin_c[G * kW];
   __shared__ float fin_l[G];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int quad = lane >> 2, pos = lane & 3;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int S = a.n_splits;
-
-  // ---- absorbed query: qt[h][i] = (row i of B^K, or U^K for i >= R) . q_h
-  for (int e = tid; e < G * kW; e += 256) {
-    const int h = e / kW, i = e % kW;
-    const uint16_t* row = i < kR ? a.bk + ((size_t)kvh * kR + i) * HD
-                                 : a.uk + ((size_t)kvh * kRM + (i - kR)) * HD;
-    const uint16_t* qr = a.q + ((size_t)b * a.n_q_heads + (size_t)kvh * G + h) * HD;
-    float acc = 0.f;
-#pragma unroll
-    for (int c = 0; c < HD / 8; ++c) {
-      const uint4 x = *reinterpret_cast<const uint4*>(row + c * 8);
-      const uint4 y = *reinterpret_cast<const uint4*>(qr + c * 8);
-      acc = dot2_bf16(x.x, y.x, acc);
-      acc = dot2_bf16(x.y, y.y, acc);
-      acc = dot2_bf16(x.z, y.z, acc);
-      acc = dot2_bf16(x.w, y.w, acc);
-    }
-    qt[h][i] = acc * a.scale_log2;
-  }
-  __syncthreads();
 
   const int n_keys = min(max(a.seq_len[b], 0), a.max_ctx);
   const int n_pages = (n_keys + kPage - 1) / kPage;
   int pb, pe;
   split_range(n_pages, split, S, pb, pe);
   const int32_t* pt = a.page_table + (size_t)b * a.pages_per_seq;
+  const size_t coef_page = (size_t)kPage * kR;          // elements per (page, head) of cK / cV
+  const uint16_t* ck_base = a.ck + a.coef_off;
+  const uint16_t* cv_base = a.cv + a.coef_off;
+  const int8_t* dk_base = a.dk + a.resid_off;
+  const int8_t* dv_base = a.dv + a.resid_off;
+  const uint16_t* sk_base = a.sk + a.scale_off;
+  const uint16_t* sv_base = a.sv + a.scale_off;
 
-  // V-side lane roles: C part lane (q8 = coefs 4*q8.., ph8 = pair phase),
-  // D part lane (jq = codes 8*jq.., dp = key pair)
-  const int q8 = lane & 7, ph8 = lane >> 3;
-  const int jq = lane & 1, dp = lane >> 1;
+  // Buffer resources over this call's sub-pools: every page load below is
+  // issued unconditionally, an absent page or granule with an offset past the
+  // resource's end (the hardware returns zeros and moves no data), so the
+  // loop holds a fixed number of loads and the next page stays in flight.
+  const uint32_t P = (uint32_t)a.n_phys_pages, H = (uint32_t)a.n_kv_heads;
+  const auto r_ck = rsrc(ck_base, P * H * (kPage * kR * 2));
+  const auto r_cv = rsrc(cv_base, P * H * (kPage * kR * 2));
+  const auto r_dk = rsrc(dk_base, P * H * (kGranules * 8));
+  const auto r_dv = rsrc(dv_base, P * H * (kGranules * 8));
+  const auto r_sk = rsrc(sk_base, P * H * (kPage * 2));
+  const auto r_sv = rsrc(sv_base, P * H * (kPage * 2));
+  const auto r_meta = rsrc(a.meta, P * (kPage * 2));
+  const int pt_last = max(pe - 1, 0);
 
-  float m[G], lsum[G], acc_c[G][4], acc_d[G][8];
+  // physical page of logical page pg, or -1 (past the partition, or a corrupt
+  // entry, which is never read)
+  auto phys_of = [&](int pg) {
+    const int ph = pt[min(pg, pt_last)];
+    return (pg < pe && (unsigned)ph < P) ? ph : -1;
+  };
+  // rank | granule offset << 8 of this lane's token; 0 when there is none
+  auto load_meta = [&](int pg, int ph) -> uint32_t {
+    const bool on = ph >= 0 && lane < n_keys - pg * kPage;
+    return __builtin_amdgcn_raw_buffer_load_b16(r_meta, (int)(on ? (uint32_t)(ph * kPage + lane) * 2 : kOOB),
+                                                0, 0);
+  };
+  auto load_coefs = [&](int ph, PageRegs& r) {
+    const uint32_t page_kv = (uint32_t)ph * H + kvh;
+    const uint32_t cb = ph >= 0 ? page_kv * (kPage * kR * 2) : kOOB;
+    const uint32_t sb = ph >= 0 ? page_kv * (kPage * 2) : kOOB;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = -INFINITY;
-    lsum[h] = 0.f;
+    for (int i = 0; i < 4; ++i) r.ck[i] = ld16(r_ck, cb + (i * 64 + lane) * 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc_c[h][i] = 0.f;
+    for (int i = 0; i < 4; ++i) r.cv[i] = ld16(r_cv, cb + (i * 64 + lane) * 16);
+    r.sk = ld8(r_sk, sb + quad * 8);
+    r.sv = ld8(r_sv, sb + quad * 8);
+  };
+  auto load_codes = [&](int ph, uint32_t meta, PageRegs& r) {
+    const int rank = min((int)(meta & 0xffu), kRM);
+    const int ng = (rank + 7) >> 3;                              // granules of this token
+    const uint32_t g0 = min(meta >> 8, (uint32_t)(kGranules - 2));  // stays inside the blob
+    // meta != 0 only for pages with ph >= 0
+    const uint32_t blob = ((uint32_t)ph * H + kvh) * (kGranules * 8) + g0 * 8;
+    const uint32_t o0 = ng >= 1 ? blob : kOOB, o1 = ng == 2 ? blob + 8 : kOOB;
+    r.dk[0] = ld8(r_dk, o0);
+    r.dk[1] = ld8(r_dk, o1);
+    r.dv[0] = ld8(r_dv, o0);
+    r.dv[1] = ld8(r_dv, o1);
+  };
+
+  // ---- the first page's requests go out before the query contraction
+  const int pg0 = pb + wave;
+  PageRegs bufA, bufB;
+  const int ph0 = phys_of(pg0);
+  const uint32_t meta0 = load_meta(pg0, ph0);
+  int ph_b = phys_of(pg0 + 4);
+  uint32_t meta_b = load_meta(pg0 + 4, ph_b);
+  load_coefs(ph0, bufA);
+
+  // ---- absorbed query: qt[h][i] = (row i of B^K, or U^K for i >= R) . q_h
+  for (int e = tid; e < NB * 4 * kW; e += 256) {
+    const int h = e / kW, i = e % kW;
+    float acc = 0.f;
+    if (h < G) {
+      const uint16_t* row = i < kR ? a.bk + ((size_t)kvh * kR + i) * HD
+                                   : a.uk + ((size_t)kvh * kRM + (i - kR)) * HD;
+      const uint16_t* qr = a.q + ((size_t)b * a.n_q_heads + (size_t)kvh * G + h) * HD;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc_d[h][j] = 0.f;
+      for (int c = 0; c < HD / 8; ++c) {
+        const uint4 x = *reinterpret_cast<const uint4*>(row + c * 8);
+        const uint4 y = *reinterpret_cast<const uint4*>(qr + c * 8);
+        acc = dot2_bf16(x.x, y.x, acc);
+        acc = dot2_bf16(x.y, y.y, acc);
+        acc = dot2_bf16(x.z, y.z, acc);
+        acc = dot2_bf16(x.w, y.w, acc);
+      }
+    }
+    qt[h][i] = acc * a.scale_log2;
+  }
+  load_codes(ph0, meta0, bufA);
+  __syncthreads();
+
+  // score B operands: lane (quad, pos) supplies head 4*hb + pos, entries
+  // 4m..4m+3 of q~ (m < 8) or u~ (m >= 8)
+  uint32_t bq_hi[NB][12][2], bq_lo[NB][12][2];
+#pragma unroll
+  for (int hb = 0; hb < NB; ++hb)
+#pragma unroll
+    for (int m = 0; m < 12; ++m)
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const float x0 = qt[hb * 4 + pos][4 * m + 2 * e2];
+        const float x1 = qt[hb * 4 + pos][4 * m + 2 * e2 + 1];
+        const uint32_t hi = pack_bf16(x0, x1);
+        bq_hi[hb][m][e2] = hi;
+        bq_lo[hb][m][e2] = pack_bf16(x0 - dev::bf16_lo(hi), x1 - dev::bf16_hi(hi));
+      }
+
+  // byte-transpose selectors of this lane
+  const uint32_t sel1 = (pos & 2) ? 0x03020706u : 0x05040100u;
+  const uint32_t sel2 = (pos & 1) ? 0x03070105u : 0x06020400u;
+
+  float m_run[NB], l_run[NB];
+  f4_t acc[NB][12];
+#pragma unroll
+  for (int hb = 0; hb < NB; ++hb) {
+    m_run[hb] = -INFINITY;
+    l_run[hb] = 0.f;
+#pragma unroll
+    for (int m = 0; m < 12; ++m) acc[hb][m] = f4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int pg = pb + wave; pg < pe; pg += 4) {
-    const int phys = pt[pg];
-    if ((unsigned)phys >= (unsigned)a.n_phys_pages) continue;   // corrupt entry: never read
-    const size_t page_kv = (size_t)phys * a.n_kv_heads + kvh;
-    const uint16_t* ckp = a.ck + a.coef_off + page_kv * 64 * kR;
-    const uint16_t* cvp = a.cv + a.coef_off + page_kv * 64 * kR;
-    const int8_t* dkp = a.dk + a.resid_off + page_kv * 64 * kRM;
-    const int8_t* dvp = a.dv + a.resid_off + page_kv * 64 * kRM;
-    const uint16_t* skp = a.sk + a.scale_off + page_kv * 64;
-    const uint16_t* svp = a.sv + a.scale_off + page_kv * 64;
-    const uint8_t* rkp = a.rank + (size_t)phys * 64;
-
-    // all loads of the page up front
-    uint4 ckr[4];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) ckr[cc] = *reinterpret_cast<const uint4*>(ckp + (cc * 64 + lane) * 8);
-    const uint4 dkr = *reinterpret_cast<const uint4*>(dkp + lane * 16);
-    const uint16_t skr = skp[lane];
-    const uint16_t svr = svp[lane];
-    const int r_t = rkp[lane];
-    uint4 cvr[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      cvr[k] = *reinterpret_cast<const uint4*>(cvp + (ph8 + 8 * k) * (kR * 2) + q8 * 8);
-    const uint4 dvr = *reinterpret_cast<const uint4*>(dvp + dp * (kRM * 2) + jq * 16);
-    const uint16_t rpair = *reinterpret_cast<const uint16_t*>(rkp + 2 * dp);
-
+  auto compute = [&](int pg, const PageRegs& r) {
     const int nvalid = n_keys - pg * kPage;
-    const bool key_ok = lane < nvalid;
-
-    // ---- scores, lane = token
-    float cf[kR], df[kRM];
+    const bool tail = nvalid < kPage;
+    // score A operands of the codes (token = lane)
+    uint32_t ad[4][2];
     {
-      const uint32_t* cw = &ckr[0].x;
+      const uint32_t w4[4] = {r.dk[0].x, r.dk[0].y, r.dk[1].x, r.dk[1].y};
 #pragma unroll
-      for (int w = 0; w < 16; ++w) {
-        cf[2 * w] = dev::bf16_lo(cw[w]);
-        cf[2 * w + 1] = dev::bf16_hi(cw[w]);
+      for (int m = 0; m < 4; ++m) codes_to_bf16(w4[m], ad[m][0], ad[m][1]);
+    }
+    const uint32_t* cw = &r.ck[0].x;    // coefficient pairs 0..15 of token `lane`
+    // value B operands of the codes: the quad's 4 tokens of code 4m + pos
+    uint32_t bd[4][2];
+    {
+      const uint32_t w4[4] = {r.dv[0].x, r.dv[0].y, r.dv[1].x, r.dv[1].y};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) codes_to_bf16(quad_transpose(w4[m], sel1, sel2), bd[m][0], bd[m][1]);
+    }
+    uint32_t bc[8][2];
+    {
+      const uint32_t* vw = &r.cv[0].x;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        bc[m][0] = vw[2 * m];
+        bc[m][1] = vw[2 * m + 1];
       }
-      const uint32_t* dw = &dkr.x;
+    }
+    // which of the quad's tokens lie before the sequence end
+    bool ok[4];
 #pragma unroll
-      for (int j = 0; j < kRM; ++j) {
-        const int v = (int)(int8_t)((dw[j / 4] >> (8 * (j % 4))) & 0xff);
-        df[j] = j < r_t ? (float)v : 0.f;
+    for (int e = 0; e < 4; ++e) ok[e] = !tail || quad * 4 + e < nvalid;
+    const uint32_t mk0 = (ok[0] ? 0x0000ffffu : 0u) | (ok[1] ? 0xffff0000u : 0u);
+    const uint32_t mk1 = (ok[2] ? 0x0000ffffu : 0u) | (ok[3] ? 0xffff0000u : 0u);
+    if (tail) {
+      // unwritten pool memory may hold NaN patterns: zero those tokens' values
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        bc[m][0] &= mk0;
+        bc[m][1] &= mk1;
       }
     }
-    const float sKf = half_to_float(skr);
-    float sc[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float zc = 0.f, zd = 0.f;
-#pragma unroll
-      for (int i = 0; i < kR; ++i) zc = fmaf(cf[i], qt[h][i], zc);
-#pragma unroll
-      for (int j = 0; j < kRM; ++j) zd = fmaf(df[j], qt[h][kR + j], zd);
-      const float z = fmaf(sKf, zd, zc);
-      sc[h] = key_ok ? z : -INFINITY;
-    }
+    float skf[4], svf[4];
+    skf[0] = half_to_float((uint16_t)(r.sk.x & 0xffffu));
+    skf[1] = half_to_float((uint16_t)(r.sk.x >> 16));
+    skf[2] = half_to_float((uint16_t)(r.sk.y & 0xffffu));
+    skf[3] = half_to_float((uint16_t)(r.sk.y >> 16));
+    svf[0] = half_to_float((uint16_t)(r.sv.x & 0xffffu));
+    svf[1] = half_to_float((uint16_t)(r.sv.x >> 16));
+    svf[2] = half_to_float((uint16_t)(r.sv.y & 0xffffu));
+    svf[3] = half_to_float((uint16_t)(r.sv.y >> 16));
 
-    // ---- online softmax; p and p*s^V to LDS as bf16 key pairs
-    const float sVf = key_ok ? half_to_float(svr) : 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mt = dev::wave_max(sc[h]);
-      const float mn = fmaxf(m[h], mt);
-      const float alpha = dev::fast_exp2(m[h] - mn);
-      m[h] = mn;
-      const uint32_t pbits = dev::f32_to_bf16_bits(dev::fast_exp2(sc[h] - mn));
-      const float p = __uint_as_float(pbits << 16);
-      lsum[h] = fmaf(lsum[h], alpha, p);
-      reinterpret_cast<uint16_t*>(p_lds[wave])[((lane >> 1) * G + h) * 2 + (lane & 1)] = (uint16_t)pbits;
-      reinterpret_cast<uint16_t*>(ps_lds[wave])[((lane >> 1) * G + h) * 2 + (lane & 1)] =
-          (uint16_t)dev::f32_to_bf16_bits(p * sVf);
+    for (int hb = 0; hb < NB; ++hb) {
+      // ---- scores: rows = the quads' tokens, columns = heads
+      // six independent accumulator chains of four products each, so that
+      // consecutive products never wait on each other's result
+      f4_t zc[4], zd[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc_c[h][i] *= alpha;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) acc_d[h][j] *= alpha;
-    }
-    __builtin_amdgcn_wave_barrier();
-
-    // ---- coefficient-space accumulation
-    if (nvalid < kPage) {   // unwritten pool memory past the sequence end may hold NaN patterns
+      for (int c = 0; c < 4; ++c) zc[c] = f4_t{0.f, 0.f, 0.f, 0.f};
+      zd[0] = zd[1] = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int key0 = 2 * (ph8 + 8 * k);
-        const uint32_t mk = (key0 < nvalid ? 0x0000ffffu : 0u) | (key0 + 1 < nvalid ? 0xffff0000u : 0u);
-        cvr[k].x &= mk; cvr[k].y &= mk; cvr[k].z &= mk; cvr[k].w &= mk;
+        const int m0 = 2 * k, m1 = 2 * k + 1;
+        zc[0] = mfma4(cw[2 * m0], cw[2 * m0 + 1], bq_hi[hb][m0][0], bq_hi[hb][m0][1], zc[0]);
+        zc[1] = mfma4(cw[2 * m1], cw[2 * m1 + 1], bq_hi[hb][m1][0], bq_hi[hb][m1][1], zc[1]);
+        zc[2] = mfma4(cw[2 * m0], cw[2 * m0 + 1], bq_lo[hb][m0][0], bq_lo[hb][m0][1], zc[2]);
+        zc[3] = mfma4(cw[2 * m1], cw[2 * m1 + 1], bq_lo[hb][m1][0], bq_lo[hb][m1][1], zc[3]);
+        zd[0] = mfma4(ad[k][0], ad[k][1], bq_hi[hb][8 + k][0], bq_hi[hb][8 + k][1], zd[0]);
+        zd[1] = mfma4(ad[k][0], ad[k][1], bq_lo[hb][8 + k][0], bq_lo[hb][8 + k][1], zd[1]);
       }
+      const bool head_ok = hb * 4 + pos < G;
+      float z[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = fmaf(skf[e], zd[0][e] + zd[1][e], (zc[0][e] + zc[1][e]) + (zc[2][e] + zc[3][e]));
+        z[e] = (ok[e] && head_ok) ? v : -INFINITY;
+      }
+      // ---- online softmax with one running max per head (uniform over the wave)
+      const float mt = quad_column_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
+      const float mn = fmaxf(m_run[hb], mt);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      // 1 exactly while the max holds (also for heads past G, whose max stays -inf)
+      const float alpha = m_run[hb] == mn ? 1.f : dev::fast_exp2(m_run[hb] - mu);
+      m_run[hb] = mn;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+        // accumulator entry e of every lane belongs to head e of the block:
+        // broadcast head e's factor from the quad
+        const int ai = __float_as_int(alpha);
+        const float a0 = __int_as_float(__builtin_amdgcn_mov_dpp(ai, 0x00, 0xf, 0xf, true));
+        const float a1 = __int_as_float(__builtin_amdgcn_mov_dpp(ai, 0x55, 0xf, 0xf, true));
+        const float a2 = __int_as_float(__builtin_amdgcn_mov_dpp(ai, 0xAA, 0xf, 0xf, true));
+        const float a3 = __int_as_float(__builtin_amdgcn_mov_dpp(ai, 0xFF, 0xf, 0xf, true));
+#pragma unroll
+        for (int m = 0; m < 12; ++m) {
+          acc[hb][m][0] *= a0;
+          acc[hb][m][1] *= a1;
+          acc[hb][m][2] *= a2;
+          acc[hb][m][3] *= a3;
+        }
+        l_run[hb] *= alpha;
+      }
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = dev::fast_exp2(z[e] - mu);
+      const uint32_t ap0 = pack_bf16(p[0], p[1]), ap1 = pack_bf16(p[2], p[3]);
+      // the bf16 probabilities enter both the numerator and the sum
+      const float q0 = dev::bf16_lo(ap0), q1 = dev::bf16_hi(ap0);
+      const float q2 = dev::bf16_lo(ap1), q3 = dev::bf16_hi(ap1);
+      l_run[hb] += (q0 + q1) + (q2 + q3);
+      // p * s^V; masked tokens (p = 0) must not pick up a NaN scale
+      const uint32_t as0 = pack_bf16(q0 * svf[0], q1 * svf[1]) & mk0;
+      const uint32_t as1 = pack_bf16(q2 * svf[2], q3 * svf[3]) & mk1;
+      // ---- values: rows = heads, columns = coefficients, k = the quad's tokens
+#pragma unroll
+      for (int m = 0; m < 8; ++m) acc[hb][m] = mfma4(ap0, ap1, bc[m][0], bc[m][1], acc[hb][m]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[hb][8 + m] = mfma4(as0, as1, bd[m][0], bd[m][1], acc[hb][8 + m]);
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int p = ph8 + 8 * k;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint32_t pp = p_lds[wave][p * G + h];
-        acc_c[h][0] = dot2_bf16(pp, cvr[k].x, acc_c[h][0]);
-        acc_c[h][1] = dot2_bf16(pp, cvr[k].y, acc_c[h][1]);
-        acc_c[h][2] = dot2_bf16(pp, cvr[k].z, acc_c[h][2]);
-        acc_c[h][3] = dot2_bf16(pp, cvr[k].w, acc_c[h][3]);
-      }
-    }
-    {
-      const int r0 = rpair & 0xff, r1 = rpair >> 8;     // ranks of keys 2dp, 2dp+1
-      const uint32_t* dw = &dvr.x;
-      uint32_t dpair[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int j = 8 * jq + jj;
-        const uint32_t two = (dw[jj / 2] >> (16 * (jj % 2))) & 0xffffu;   // (key 2dp, key 2dp+1)
-        const int v0 = (int)(int8_t)(two & 0xff), v1 = (int)(int8_t)(two >> 8);
-        dpair[jj] = (j < r0 ? i8_to_bf16(v0) : 0u) | ((j < r1 ? i8_to_bf16(v1) : 0u) << 16);
-      }
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const uint32_t pp = ps_lds[wave][dp * G + h];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) acc_d[h][jj] = dot2_bf16(pp, dpair[jj], acc_d[h][jj]);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
+  };
+
+  // ---- main loop over this wave's pages pg0, pg0+4, ...: two page buffers,
+  // the next page's loads issued before the current page is computed, the
+  // page after next's meta one step earlier still
+  for (int pg = pg0; pg < pe; pg += 8) {
+    const int ph_c = phys_of(pg + 8);
+    const uint32_t meta_c = load_meta(pg + 8, ph_c);
+    load_coefs(ph_b, bufB);
+    load_codes(ph_b, meta_b, bufB);
+    compute(pg, bufA);
+    if (pg + 4 >= pe) break;
+    ph_b = phys_of(pg + 12);
+    meta_b = load_meta(pg + 12, ph_b);
+    load_coefs(ph_c, bufA);
+    load_codes(ph_c, meta_c, bufA);
+    compute(pg + 4, bufB);
   }
 
-  // ---- this wave's (coefficient sums, m, l) to LDS
+  // ---- this wave's per-head (coefficient sums, m, l) to LDS
+  const int row = lane >> 4;
+  const bool writer = (lane & 15) < 4;          // lanes 16*row + pos
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float l = dev::wave_sum(lsum[h]);
+  for (int hb = 0; hb < NB; ++hb) {
+    const float l = quad_row_sum(l_run[hb]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x = acc_c[h][i];
-      x += __shfl_xor(x, 8);
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      if (lane < 8) mrg_c[wave][h][4 * q8 + i] = x;
-    }
+    for (int m = 0; m < 12; ++m)
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      float x = acc_d[h][jj];
-#pragma unroll
-      for (int off = 2; off < 64; off <<= 1) x += __shfl_xor(x, off);
-      if (lane < 2) mrg_c[wave][h][kR + 8 * jq + jj] = x;
-    }
-    if (lane == 0) {
-      mrg_m[wave][h] = m[h];
-      mrg_l[wave][h] = l;
-    }
+      for (int e = 0; e < 4; ++e) {
+        const float x = quad_row_sum(acc[hb][m][e]);
+        if (writer) part[wave][row][hb * 4 + e][4 * m + pos] = x;
+      }
+    if (writer) part_l[wave][row][hb * 4 + pos] = l;
+    if (lane < 4) wave_m[wave][hb * 4 + lane] = m_run[hb];
   }
   __syncthreads();
 
+  // ---- merge the 4 waves; write the output (S == 1) or the partition
   const size_t hq0 = (size_t)b * a.n_q_heads + (size_t)kvh * G;
   for (int e = tid; e < G * kW; e += 256) {
     const int h = e / kW, i = e % kW;
-    float M = mrg_m[0][h];
+    float M = wave_m[0][h];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, mrg_m[w][h]);
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, wave_m[w][h]);
     float c = 0.f, l = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float f = dev::fast_exp2(mrg_m[w][h] - M);
-        c = fmaf(f, mrg_c[w][h][i], c);
-        l = fmaf(f, mrg_l[w][h], l);
+        const float f = dev::fast_exp2(wave_m[w][h] - M);
+        const float cw = (part[w][0][h][i] + part[w][1][h][i]) + (part[w][2][h][i] + part[w][3][h][i]);
+        const float lw = (part_l[w][0][h] + part_l[w][1][h]) + (part_l[w][2][h] + part_l[w][3][h]);
+        c = fmaf(f, cw, c);
+        l = fmaf(f, lw, l);
       }
     }
     if (S == 1) {
       fin_c[e] = c;
       if (i == 0) fin_l[h] = l;
     } else {
-      const size_t row = (hq0 + h) * S + split;
-      a.ws_c[row * kW + i] = c;
+      const size_t rw = (hq0 + h) * S + split;
+      a.ws_c[rw * kW + i] = c;
       if (i == 0) {
-        a.ws_m[row] = M;
-        a.ws_l[row] = l;
+        a.ws_m[rw] = M;
+        a.ws_l[rw] = l;
       }
     }
   }
@@ -359,25 +543,20 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
 }
 
 // Merge of S partitions in coefficient space, then the basis projection.
-// Every partition writes its row (an empty one as c = 0, m = -inf, l = 0).
-// Loads that do not depend on each other are issued together: the maxima and
-// sums to LDS, each thread's basis column (its d is fixed: 256 is a multiple
-// of HD) into registers, then the S coefficient partials.
+// Every partition writes its row (an empty one as c = 0, m = -inf, l = 0), so
+// a thread loads its S (m, l, c) triples 16 at a time with no dependence
+// between them and folds each batch into a running (M, c, l); the basis
+// column each thread projects with (its d is fixed: 256 is a multiple of HD)
+// is loaded up front.  Partition order is fixed: deterministic.
 template <int HD, int G>
 __global__ __launch_bounds__(256) void fact_merge_kernel(FactParams a) {
   static_assert(256 % HD == 0, "a thread keeps one output column");
-  __shared__ float m_lds[G * kMaxSplitsF];
-  __shared__ float l_lds[G * kMaxSplitsF];
   __shared__ float den[G];
   __shared__ float coef[G * kW];
   const int tid = threadIdx.x;
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int S = a.n_splits;
   const size_t hq0 = (size_t)b * a.n_q_heads + (size_t)kvh * G;
-  for (int i = tid; i < G * S; i += 256) {
-    m_lds[i] = a.ws_m[hq0 * S + i];
-    l_lds[i] = a.ws_l[hq0 * S + i];
-  }
   const int d = tid % HD;
   float col[kW];   // column d of B^V (rows 0..R-1) then U^V (rows R..R+RM-1)
   {
@@ -388,23 +567,38 @@ __global__ __launch_bounds__(256) void fact_merge_kernel(FactParams a) {
 #pragma unroll
     for (int j = 0; j < kRM; ++j) col[kR + j] = __uint_as_float((uint32_t)uv[j * HD] << 16);
   }
-  __syncthreads();
   for (int e = tid; e < G * kW; e += 256) {
     const int h = e / kW, i = e % kW;
-    const float* ml = m_lds + h * S;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[s]);
-    const float* c = a.ws_c + (hq0 + h) * S * kW + i;
-    float acc = 0.f, l = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll 8
-      for (int s = 0; s < S; ++s) {
-        const float f = dev::fast_exp2(ml[s] - M);   // 0 for an empty partition
-        acc = fmaf(f, c[(size_t)s * kW], acc);
-        l = fmaf(f, l_lds[h * S + s], l);
+    const float* mrow = a.ws_m + (hq0 + h) * S;
+    const float* lrow = a.ws_l + (hq0 + h) * S;
+    const float* crow = a.ws_c + (hq0 + h) * S * kW + i;
+    float M = -INFINITY, c = 0.f, l = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 16) {
+      float mv[16], lv[16], cv[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int s = min(s0 + k, S - 1);
+        mv[k] = s0 + k < S ? mrow[s] : -INFINITY;
+        lv[k] = lrow[s];
+        cv[k] = crow[(size_t)s * kW];
+      }
+      float Mn = M;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) Mn = fmaxf(Mn, mv[k]);
+      if (Mn != -INFINITY) {
+        const float r = dev::fast_exp2(M - Mn);   // 0 while M is -inf
+        c *= r;
+        l *= r;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float f = dev::fast_exp2(mv[k] - Mn);   // 0 for empty or absent partitions
+          c = fmaf(f, cv[k], c);
+          l = fmaf(f, lv[k], l);
+        }
+        M = Mn;
       }
     }
-    coef[e] = acc;
+    coef[e] = c;
     if (i == 0) den[h] = l;
   }
   __syncthreads();
@@ -450,6 +644,9 @@ FactFn pick(int hd, int G) {
 
 // ---------------------------------------------------------------- writes
 
+// One thread per (sequence, token, KV head).  A token's granule offset is the
+// sum of ceil(r/8) over the page's earlier tokens: ranks of tokens this call
+// writes come from `rank`, earlier ones from the page's meta entries.
 __global__ __launch_bounds__(256) void fact_append_kernel(FactAppendLaunch a) {
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)a.batch * a.n * a.n_kv_heads;
@@ -458,15 +655,24 @@ __global__ __launch_bounds__(256) void fact_append_kernel(FactAppendLaunch a) {
   const long long bi = idx / a.n_kv_heads;
   const int i = (int)(bi % a.n);
   const int b = (int)(bi / a.n);
-  const int pos = a.start_pos[b] + i;
+  const int sp = a.start_pos[b];
+  const int pos = sp + i;
   if (pos < 0 || pos >= a.max_ctx) return;
   const int page = a.page_table[(size_t)b * a.pages_per_seq + pos / kPage];
   if (page < 0 || page >= a.n_phys_pages) return;
   const int t = pos % kPage;
   const size_t page_kv = (size_t)page * a.n_kv_heads + kvh;
   const size_t src_row = ((size_t)b * a.n + i) * a.n_kv_heads + kvh;
+  const uint8_t* rk = a.rank + (size_t)b * a.n;
+  uint16_t* meta = static_cast<uint16_t*>(a.rank_pool) + (size_t)page * kPage;
+  const int r = min((int)rk[i], kRM);
+  int g0 = 0;
+  for (int u = 0, pu = pos - t; u < t; ++u, ++pu) {
+    const int ru = pu >= sp ? (int)rk[pu - sp] : (int)(meta[u] & 0xffu);
+    g0 += (min(ru, kRM) + 7) >> 3;
+  }
   if (a.coef_slot >= 0) {
-    const size_t base = ((size_t)a.coef_slot * a.n_phys_pages * a.n_kv_heads + page_kv) * 64 * kR;
+    const size_t base = ((size_t)a.coef_slot * a.n_phys_pages * a.n_kv_heads + page_kv) * kPage * kR;
     const uint16_t* ck = static_cast<const uint16_t*>(a.ck) + src_row * kR;
     const uint16_t* cv = static_cast<const uint16_t*>(a.cv) + src_row * kR;
     uint16_t* dk = static_cast<uint16_t*>(a.ck_pool) + base;
@@ -475,23 +681,37 @@ __global__ __launch_bounds__(256) void fact_append_kernel(FactAppendLaunch a) {
     for (int cc = 0; cc < 4; ++cc)
       *reinterpret_cast<uint4*>(dk + (cc * 64 + t) * 8) = *reinterpret_cast<const uint4*>(ck + cc * 8);
 #pragma unroll 8
-    for (int e = 0; e < kR; ++e) dv[(t >> 1) * (kR * 2) + e * 2 + (t & 1)] = cv[e];
+    for (int e = 0; e < kR; ++e) {
+      const int m = e >> 2, ln = ((t >> 2) << 2) | (e & 3);
+      dv[((m >> 1) * 64 + ln) * 8 + (m & 1) * 4 + (t & 3)] = cv[e];
+    }
   }
   {
     const size_t lbase = (size_t)a.layer * a.n_phys_pages * a.n_kv_heads + page_kv;
-    int8_t* dk = static_cast<int8_t*>(a.dk_pool) + lbase * 64 * kRM;
-    int8_t* dv = static_cast<int8_t*>(a.dv_pool) + lbase * 64 * kRM;
-    *reinterpret_cast<uint4*>(dk + t * kRM) = *reinterpret_cast<const uint4*>(a.dk + src_row * kRM);
-    const int8_t* sv = a.dv + src_row * kRM;
+    const int ng = (r + 7) >> 3;
+    // codes j >= r are stored as zero
+    uint32_t keep[4];
 #pragma unroll
-    for (int j = 0; j < kRM; ++j) dv[(t >> 1) * (kRM * 2) + j * 2 + (t & 1)] = sv[j];
-    static_cast<uint16_t*>(a.sk_pool)[lbase * 64 + t] = static_cast<const uint16_t*>(a.sk)[src_row];
-    static_cast<uint16_t*>(a.sv_pool)[lbase * 64 + t] = static_cast<const uint16_t*>(a.sv)[src_row];
+    for (int w = 0; w < 4; ++w) {
+      const int nb = min(max(r - 4 * w, 0), 4);
+      keep[w] = nb == 4 ? 0xffffffffu : ((1u << (8 * nb)) - 1u);
+    }
+    const uint4 ck = *reinterpret_cast<const uint4*>(a.dk + src_row * kRM);
+    const uint4 cv = *reinterpret_cast<const uint4*>(a.dv + src_row * kRM);
+    int8_t* dk = static_cast<int8_t*>(a.dk_pool) + lbase * (kGranules * 8) + (size_t)g0 * 8;
+    int8_t* dv = static_cast<int8_t*>(a.dv_pool) + lbase * (kGranules * 8) + (size_t)g0 * 8;
+    if (ng >= 1) {
+      *reinterpret_cast<uint2*>(dk) = make_uint2(ck.x & keep[0], ck.y & keep[1]);
+      *reinterpret_cast<uint2*>(dv) = make_uint2(cv.x & keep[0], cv.y & keep[1]);
+    }
+    if (ng == 2) {
+      *reinterpret_cast<uint2*>(dk + 8) = make_uint2(ck.z & keep[2], ck.w & keep[3]);
+      *reinterpret_cast<uint2*>(dv + 8) = make_uint2(cv.z & keep[2], cv.w & keep[3]);
+    }
+    static_cast<uint16_t*>(a.sk_pool)[lbase * kPage + t] = static_cast<const uint16_t*>(a.sk)[src_row];
+    static_cast<uint16_t*>(a.sv_pool)[lbase * kPage + t] = static_cast<const uint16_t*>(a.sv)[src_row];
   }
-  if (a.rank && kvh == 0) {
-    const uint8_t r = a.rank[(size_t)b * a.n + i];
-    static_cast<uint8_t*>(a.rank_pool)[(size_t)page * 64 + t] = r > kRM ? (uint8_t)kRM : r;
-  }
+  if (kvh == 0) meta[t] = (uint16_t)(r | (g0 << 8));
 }
 
 }  // namespace
@@ -513,7 +733,7 @@ int launch_fact_decode(const FactDecodeLaunch& a, void* stream) {
   p.dv = static_cast<const int8_t*>(a.dv_pool);
   p.sk = static_cast<const uint16_t*>(a.sk_pool);
   p.sv = static_cast<const uint16_t*>(a.sv_pool);
-  p.rank = static_cast<const uint8_t*>(a.rank_pool);
+  p.meta = static_cast<const uint16_t*>(a.rank_pool);
   const size_t Hkv = a.n_kv_heads;
   p.bk = static_cast<const uint16_t*>(a.basis_k) + (size_t)a.coef_slot * Hkv * kR * a.head_dim;
   p.bv = static_cast<const uint16_t*>(a.basis_v) + (size_t)a.coef_slot * Hkv * kR * a.head_dim;
@@ -524,9 +744,9 @@ int launch_fact_decode(const FactDecodeLaunch& a, void* stream) {
   p.n_phys_pages = a.n_phys_pages;
   p.n_kv_heads = a.n_kv_heads;
   p.n_q_heads = a.n_q_heads;
-  p.coef_off = (int64_t)a.coef_slot * a.n_phys_pages * a.n_kv_heads * 64 * kR;
-  p.resid_off = (int64_t)a.layer * a.n_phys_pages * a.n_kv_heads * 64 * kRM;
-  p.scale_off = (int64_t)a.layer * a.n_phys_pages * a.n_kv_heads * 64;
+  p.coef_off = (int64_t)a.coef_slot * a.n_phys_pages * a.n_kv_heads * kPage * kR;
+  p.resid_off = (int64_t)a.layer * a.n_phys_pages * a.n_kv_heads * kGranules * 8;
+  p.scale_off = (int64_t)a.layer * a.n_phys_pages * a.n_kv_heads * kPage;
   p.q = static_cast<const uint16_t*>(a.q);
   p.seq_len = a.seq_len;
   p.max_ctx = a.max_ctx;

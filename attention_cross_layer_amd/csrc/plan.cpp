@@ -158,7 +158,7 @@ extern "C" kvs_status kvs_cache_layout(const kvs_plan* plan, kvs_cache_sizes* ou
     out->coef_pool_bytes = size_t(p.n_slots) * page_rows * c.basis_rank * 2;
     out->resid_pool_bytes = size_t(c.n_layers) * page_rows * c.resid_rank_max;
     out->scale_pool_bytes = size_t(c.n_layers) * page_rows * 2;
-    out->rank_pool_bytes = size_t(p.n_phys_pages) * kPage;
+    out->rank_pool_bytes = size_t(p.n_phys_pages) * kPage * 2;
     out->basis_bytes = size_t(p.n_slots) * c.n_kv_heads * c.basis_rank * c.head_dim * 2;
     out->resid_basis_bytes = size_t(c.n_layers) * c.n_kv_heads * c.resid_rank_max * c.head_dim * 2;
   }

@@ -107,8 +107,7 @@ def setup_factorized(wl):
         uk_all[l].copy_(uk)
         uv_all[l].copy_(uv)
         dk, dv, sk, sv = datagen.layer_residual(wl, l, rank, device="cuda")
-        K.kvs_append_factorized(plan, cache, l, ck, cv, dk, dv, sk, sv,
-                                rank if l == 0 else None, zeros)
+        K.kvs_append_factorized(plan, cache, l, ck, cv, dk, dv, sk, sv, rank, zeros)
     torch.cuda.synchronize()
     return src, w, plan, cache, owners, rank
 
@@ -415,8 +414,8 @@ def main():
 
         def append(l):
             ck, cv, dk, dv, sk, sv = new_f[l]
-            K.kvs_append_factorized(plan, cache, l, ck, cv, dk, dv, sk, sv,
-                                    r1 if l == 0 else None, pos, stream=stream)
+            K.kvs_append_factorized(plan, cache, l, ck, cv, dk, dv, sk, sv, r1, pos,
+                                    stream=stream)
         call_bytes = [fact_bytes_per_call(wl, rank)] * L
     else:
         new_kv = {l: datagen.owner_kv(wl, 1000 + l, device="cuda", ctx=1) for l in owners}

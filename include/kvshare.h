@@ -113,13 +113,20 @@ typedef struct {
  *   dense V pool  [n_slots][n_phys_pages][Hkv][32][hd][2]     token pairs
  *                 (element (t, d) of a page at (t/2)*hd*2 + d*2 + t%2)
  *   page table    [max_batch][pages_per_seq] int32 in [0, n_phys_pages)
- *   factorized:
- *     cK / cV     [n_slots][n_phys_pages][Hkv][64][R]          bf16
- *     dK / dV     [n_layers][n_phys_pages][Hkv][64][Rmax]      int8
- *     sK / sV     [n_layers][n_phys_pages][Hkv][64]            fp16
- *     rank        [n_phys_pages][64]                           uint8
- *     BK / BV     [n_slots][Hkv][R][hd]                        bf16
- *     UK / UV     [n_layers][Hkv][Rmax][hd]                    bf16       */
+ *   factorized (R = 32, Rmax = 16), per (page, KV head):
+ *     cK   [n_slots][n_phys_pages][Hkv][4][64][8] bf16: coefficients
+ *          8c..8c+7 of token t at (c*64 + t)*8
+ *     cV   [n_slots][n_phys_pages][Hkv][4][64][2][4] bf16: coefficient i of
+ *          token t at ((m/2)*64 + 4*(t/4) + i%4)*8 + (m%2)*4 + t%4, m = i/4
+ *     dK / dV  [n_layers][n_phys_pages][Hkv][128][8] int8: rank-packed code
+ *          granules; token t owns ceil(r_t/8) granules starting at granule
+ *          o_t = sum over the page's earlier tokens of ceil(r/8); codes
+ *          j >= r_t inside them are zero
+ *     sK / sV  [n_layers][n_phys_pages][Hkv][64] fp16
+ *     rank (the meta pool) [n_phys_pages][64] uint16 = r_t | o_t << 8 (shared
+ *          by all layers and heads)
+ *     BK / BV  [n_slots][Hkv][R][hd] bf16;  UK / UV  [n_layers][Hkv][Rmax][hd]
+ *          bf16 (written by the caller)                                    */
 typedef struct {
   int32_t page_tokens;         /* 64                                           */
   int32_t pages_per_seq;       /* ceil(max_ctx / 64)                           */
@@ -131,7 +138,7 @@ typedef struct {
   size_t  coef_pool_bytes;     /* factorized: each of cK, cV                   */
   size_t  resid_pool_bytes;    /* factorized: each of dK, dV                   */
   size_t  scale_pool_bytes;    /* factorized: each of sK, sV                   */
-  size_t  rank_pool_bytes;     /* factorized                                   */
+  size_t  rank_pool_bytes;     /* factorized: the meta pool (rank, offset)     */
   size_t  basis_bytes;         /* factorized: each of BK, BV                   */
   size_t  resid_basis_bytes;   /* factorized: each of UK, UV                   */
 } kvs_cache_sizes;
@@ -206,11 +213,16 @@ KVS_API kvs_status kvs_append(const kvs_plan* plan, const kvs_cache* cache, int3
  *   ck, cv     device bf16 [batch][n][Hkv][R]: the pair coefficients; given
  *              only by the layer that owns the pair's slot (else NULL)
  *   dk, dv     device int8 [batch][n][Hkv][Rmax]; codes at j >= r_t are
- *              stored but never read
+ *              ignored (stored as zero)
  *   sk, sv     device fp16 [batch][n][Hkv]
- *   rank       device uint8 [batch][n] in [0, Rmax], or NULL to leave the
- *              stored ranks unchanged (ranks are per token, shared by layers)
- *   start_pos  as for kvs_append. */
+ *   rank       device uint8 [batch][n] (values above Rmax count as Rmax);
+ *              required on every call: a token's codes are placed after those
+ *              of the page's earlier tokens, so tokens of a page are appended
+ *              in position order and a token's rank, shared by all layers,
+ *              never changes once written
+ *   start_pos  as for kvs_append.
+ * Errors as for kvs_append; ck given for a layer that does not own its pair's
+ * slot -> KVS_ERR_NOT_SOURCE. */
 KVS_API kvs_status kvs_append_factorized(const kvs_plan* plan, const kvs_cache* cache,
                                          int32_t layer, const void* ck, const void* cv,
                                          const int8_t* dk, const int8_t* dv,

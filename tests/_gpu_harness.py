@@ -153,7 +153,7 @@ class Factorized:
                     None if coefs is None else coefs[1][:, :n].contiguous().cuda(),
                     dk[:, :n].contiguous().cuda(), dv[:, :n].contiguous().cuda(),
                     sk[:, :n].contiguous().cuda(), sv[:, :n].contiguous().cuda(),
-                    self.rank[:, :n].contiguous().cuda() if l == 0 else None, sp.cuda())
+                    self.rank[:, :n].contiguous().cuda(), sp.cuda())
         torch.cuda.synchronize()
 
     def q(self, layer):

@@ -78,3 +78,67 @@ def test_factorized_full_size_sampled():
         max_abs, rel = errors(got[1:2], ref)
         note(f"   layer {l}: max_abs {max_abs:.2e} rel {rel:.2e}")
         assert max_abs <= 1e-2 and rel <= 5e-3
+
+
+def test_factorized_append_layout_bit_exact():
+    """Pool bytes after two appends (the second starting mid-page, so granule
+    offsets come partly from stored ranks) equal the documented layout:
+    cK chunk-major, cV quad-interleaved, rank-packed code granules with zeros
+    past each rank, meta = rank | granule offset << 8."""
+    wl = F.with_(n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    B, ctx, n1, n2 = 2, 192, 100, 70
+    import attention_cross_layer_amd as K
+    src, w = datagen.share_map(wl)
+    cfg = K.make_config(wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, "bf16", B, ctx,
+                        kind=K.KVS_FACTORIZED, basis_rank=32, resid_rank_max=16)
+    plan = K.kvs_share_plan(cfg, src, w)
+    c = K.Cache(plan, "cuda")
+    for t in (c.ck_pool, c.cv_pool, c.dk_pool, c.dv_pool, c.rank_pool):
+        t.zero_()
+    g = torch.Generator().manual_seed(7)
+    n = n1 + n2
+    rank = torch.randint(0, 17, (B, n), generator=g).to(torch.uint8)
+    ck = torch.randn(B, n, 2, 32, generator=g).to(torch.bfloat16)
+    cv = torch.randn(B, n, 2, 32, generator=g).to(torch.bfloat16)
+    dk = torch.randint(-127, 128, (B, n, 2, 16), generator=g).to(torch.int8)
+    dv = torch.randint(-127, 128, (B, n, 2, 16), generator=g).to(torch.int8)
+    sk = torch.rand(B, n, 2, generator=g).to(torch.float16)
+    sv = torch.rand(B, n, 2, generator=g).to(torch.float16)
+    for lo, hi in ((0, n1), (n1, n)):
+        sp = torch.full((B,), lo, dtype=torch.int32).cuda()
+        K.kvs_append_factorized(plan, c, 0, ck[:, lo:hi].contiguous().cuda(),
+                                cv[:, lo:hi].contiguous().cuda(), dk[:, lo:hi].contiguous().cuda(),
+                                dv[:, lo:hi].contiguous().cuda(), sk[:, lo:hi].contiguous().cuda(),
+                                sv[:, lo:hi].contiguous().cuda(), rank[:, lo:hi].contiguous().cuda(), sp)
+    torch.cuda.synchronize()
+    sz = c.sizes
+    P = sz.n_phys_pages
+    pt = c.page_table.cpu().view(B, -1)
+    ckp = c.ck_pool.cpu().view(torch.int16).view(-1, P, 2, 64 * 32)
+    cvp = c.cv_pool.cpu().view(torch.int16).view(-1, P, 2, 64 * 32)
+    dkp = c.dk_pool.cpu().view(torch.int8).view(-1, P, 2, 128 * 8)
+    dvp = c.dv_pool.cpu().view(torch.int8).view(-1, P, 2, 128 * 8)
+    meta = c.rank_pool.cpu().view(torch.int16).view(P, 64).to(torch.int32) & 0xffff
+    ck16, cv16 = ck.view(torch.int16), cv.view(torch.int16)
+    for b in range(B):
+        goff = 0
+        for pos in range(n):
+            page, t = int(pt[b, pos // 64]), pos % 64
+            if t == 0:
+                goff = 0
+            r = int(rank[b, pos])
+            assert int(meta[page, t]) == r | (goff << 8), (b, pos)
+            for h in range(2):
+                for i in range(32):
+                    assert int(ckp[0, page, h, ((i // 8) * 64 + t) * 8 + i % 8]) == int(ck16[b, pos, h, i])
+                    m, j = i // 4, i % 4
+                    ln = 4 * (t // 4) + j
+                    off = ((m // 2) * 64 + ln) * 8 + (m % 2) * 4 + t % 4
+                    assert int(cvp[0, page, h, off]) == int(cv16[b, pos, h, i])
+                ng = (r + 7) // 8
+                for j in range(8 * ng):
+                    want_k = int(dk[b, pos, h, j]) if j < r else 0
+                    want_v = int(dv[b, pos, h, j]) if j < r else 0
+                    assert int(dkp[0, page, h, goff * 8 + j]) == want_k, (b, pos, h, j)
+                    assert int(dvp[0, page, h, goff * 8 + j]) == want_v, (b, pos, h, j)
+            goff += (r + 7) // 8
