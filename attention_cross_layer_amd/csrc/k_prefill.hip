@@ -80,9 +80,15 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x1
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return dev::f32_to_bf16_bits(lo) | (dev::f32_to_bf16_bits(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
 
 // w0*a + w1*b per bf16 element of two 16-byte chunks, rounded back to bf16.
 __device__ __forceinline__ uint4 mix_chunk(const uint4& a, const uint4& b, float w0, float w1) {
@@ -141,6 +147,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
   const bool row_ok = row < n;
   const int pos = T - n + row;                               // absolute position
   const int row_kend = !row_ok ? 0 : (a.causal ? min(T, pos + 1) : T);
+  // tiles below this one need no key mask in any row of the wave (the wave's
+  // first row has the smallest key limit; rows past n make the wave masked)
+  const int wave_kend = (i0 + kRows <= n) ? (a.causal ? min(T, T - n + i0 + 1) : T) : 0;
+  const int unmasked_tiles = wave_kend / 64;
 
   uint4 qreg[KS];
   {
@@ -224,20 +234,28 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
       }
     }
 
-    // ---- online softmax for this lane's query row
+    // ---- online softmax for this lane's query row, on raw scores (the
+    // positive scale commutes with the max); keys past the row's limit are
+    // masked only in tiles that reach a limit
+    if (t >= unmasked_tiles) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = t * 64 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
+          s[kb][r] = key < row_kend ? s[kb][r] : -INFINITY;
+        }
+    }
     float mt = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = t * 64 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
-        const float v = key < row_kend ? s[kb][r] * a.scale_log2 : -INFINITY;
-        s[kb][r] = v;
-        mt = fmaxf(mt, v);
-      }
+      for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float mn = fmaxf(m_run, mt);
-    const float alpha = mn == -INFINITY ? 1.f : dev::fast_exp2(m_run - mn);
+    // exp2(scale * (s - mn)) as one fma; a row with no key yet keeps p = 0
+    const float neg = mn == -INFINITY ? 0.f : -mn * a.scale_log2;
+    const float alpha = m_run == mn ? 1.f : dev::fast_exp2(fmaf(m_run, a.scale_log2, neg));
     m_run = mn;
     float lt = 0.f;
     uint4 pb[4];
@@ -247,25 +265,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
       for (int sh = 0; sh < 2; ++sh) {
         float p[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = s[kb][8 * sh + e];
-          p[e] = v == -INFINITY ? 0.f : dev::fast_exp2(v - mn);
-        }
+        for (int e = 0; e < 8; ++e) p[e] = dev::fast_exp2(fmaf(s[kb][8 * sh + e], a.scale_log2, neg));
         uint4 w;
         w.x = pack_bf16(p[0], p[1]);
         w.y = pack_bf16(p[2], p[3]);
         w.z = pack_bf16(p[4], p[5]);
         w.w = pack_bf16(p[6], p[7]);
-        // the running sum uses the same bf16-rounded probabilities
-        lt += dev::bf16_lo(w.x) + dev::bf16_hi(w.x) + dev::bf16_lo(w.y) + dev::bf16_hi(w.y) +
-              dev::bf16_lo(w.z) + dev::bf16_hi(w.z) + dev::bf16_lo(w.w) + dev::bf16_hi(w.w);
+        // the running sum adds the same bf16-rounded probabilities (dot with ones)
+        lt = dev::dot2_bf16(w.x, kOnesBf16x2, lt);
+        lt = dev::dot2_bf16(w.y, kOnesBf16x2, lt);
+        lt = dev::dot2_bf16(w.z, kOnesBf16x2, lt);
+        lt = dev::dot2_bf16(w.w, kOnesBf16x2, lt);
         pb[2 * kb + sh] = w;
       }
     l_run = fmaf(l_run, alpha, lt);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+    }
 
     // ---- O^T += V^T P^T; step sp covers keys 16sp + 8(e/4) + 4hh + e%4
 #pragma unroll
