@@ -50,7 +50,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 constexpr int kRows = 32;        // query rows per wave
-constexpr int kVRow = 64 + 4;    // V^T row pitch in keys (8-byte aligned, bank-spread)
+constexpr int kVRow = 64 + 8;    // V^T row pitch in keys (16-byte aligned rows)
 
 struct PrefillParams {
   const uint16_t* k_pool;
@@ -114,6 +114,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
   constexpr int MB = HD / 32;                // 32-dim blocks of O^T
   constexpr int KCH = 64 * NCH / 256;        // K chunks staged per thread per source
   constexpr int VCH = KCH;                   // V chunks staged per thread per source
+  static_assert(VCH == 2 || VCH == 4, "V staging stores 2 or 4 dwords per dim row");
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][64 * HD];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][HD * kVRow];
@@ -166,6 +167,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
   const int64_t so1 = (int64_t)a.slot1 * a.slot_stride;
 
   uint4 kst[NSRC][KCH], vst[NSRC][VCH];
+  // V chunk u of this thread: key pair (tid / (HD/4)) * VCH + u, dims
+  // 4 * (tid % (HD/4)) .. +3 (16-byte unit pair * HD/4 + dim group)
+  auto v_chunk = [&](int u) { return ((tid / (HD / 4)) * VCH + u) * (HD / 4) + tid % (HD / 4); };
   auto load_tile = [&](int t) {
     int page = pt[t];
     if ((unsigned)page >= (unsigned)a.n_phys_pages) page = 0;   // corrupt entry: read page 0, masked below
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
 #pragma unroll
       for (int u = 0; u < KCH; ++u) kst[s][u] = *reinterpret_cast<const uint4*>(kp + (tid + 256 * u) * 8);
 #pragma unroll
-      for (int u = 0; u < VCH; ++u) vst[s][u] = *reinterpret_cast<const uint4*>(vp + (tid + 256 * u) * 8);
+      for (int u = 0; u < VCH; ++u) vst[s][u] = *reinterpret_cast<const uint4*>(vp + v_chunk(u) * 8);
     }
   };
   auto store_tile = [&](int t, int buf) {
@@ -193,18 +197,31 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
       uint4 v = NSRC == 2 ? mix_chunk(kst[0][u], kst[NSRC - 1][u], a.w0, a.w1) : kst[0][u];
       *reinterpret_cast<uint4*>(&k_lds[buf][key * HD + ((c ^ (key & (NCH - 1))) * 8)]) = v;
     }
+    // V^T: this thread holds VCH consecutive key pairs of its 4 dims (a
+    // dword = one dim of a key pair), so each dim row takes one VCH-dword
+    // store, pairs in key order
+    {
+      const int L = tid % (HD / 4), q = tid / (HD / 4);
+      uint32_t w[4][VCH];
 #pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int qi = tid + 256 * u;
-      const int pair = qi / (HD / 4), d0 = 4 * (qi % (HD / 4));
-      uint4 v = NSRC == 2 ? mix_chunk(vst[0][u], vst[NSRC - 1][u], a.w0, a.w1) : vst[0][u];
-      const int k0 = key0 + 2 * pair;                         // keys k0, k0+1
-      const uint32_t mk = (page_ok && k0 < T ? 0x0000ffffu : 0u) | (page_ok && k0 + 1 < T ? 0xffff0000u : 0u);
+      for (int u = 0; u < VCH; ++u) {
+        uint4 v = NSRC == 2 ? mix_chunk(vst[0][u], vst[NSRC - 1][u], a.w0, a.w1) : vst[0][u];
+        const int k0 = key0 + 2 * (q * VCH + u);                // keys k0, k0+1
+        const uint32_t mk = (page_ok && k0 < T ? 0x0000ffffu : 0u) | (page_ok && k0 + 1 < T ? 0xffff0000u : 0u);
+        w[0][u] = v.x & mk;
+        w[1][u] = v.y & mk;
+        w[2][u] = v.z & mk;
+        w[3][u] = v.w & mk;
+      }
       uint32_t* dst = reinterpret_cast<uint32_t*>(&v_lds[buf][0]);
-      dst[((d0 + 0) * kVRow + 2 * pair) / 2] = v.x & mk;
-      dst[((d0 + 1) * kVRow + 2 * pair) / 2] = v.y & mk;
-      dst[((d0 + 2) * kVRow + 2 * pair) / 2] = v.z & mk;
-      dst[((d0 + 3) * kVRow + 2 * pair) / 2] = v.w & mk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t* row = dst + (4 * L + i) * (kVRow / 2) + q * VCH;
+        if constexpr (VCH == 4)
+          *reinterpret_cast<uint4*>(row) = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]);
+        else
+          *reinterpret_cast<uint2*>(row) = make_uint2(w[i][0], w[i][1]);
+      }
     }
   };
 
