@@ -51,7 +51,7 @@ class kvs_config(ctypes.Structure):
 class kvs_layer_info(ctypes.Structure):
     _fields_ = [("owns_kv", ctypes.c_int32), ("n_src", ctypes.c_int32),
                 ("src_layer", ctypes.c_int32 * 2), ("src_slot", ctypes.c_int32 * 2),
-                ("weight", ctypes.c_float * 2)]
+                ("weight", ctypes.c_float * 2), ("masks_current", ctypes.c_int32)]
 
 
 class kvs_plan_info(ctypes.Structure):

@@ -129,6 +129,7 @@ extern "C" kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cac
     f.q = q;
     f.seq_len = seq_len;
     f.max_ctx = p.cfg.max_ctx;
+    f.key_excl = li.masks_current;
     f.batch = batch;
     f.n_splits = n_splits;
     f.scale_log2 = scale_log2(p.cfg.head_dim);
@@ -160,6 +161,7 @@ extern "C" kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cac
   a.q = q;
   a.seq_len = seq_len;
   a.max_ctx = p.cfg.max_ctx;
+  a.key_excl = li.masks_current;
   a.batch = batch;
   a.n_splits = n_splits;
   a.scale_log2 = scale_log2(p.cfg.head_dim);
@@ -210,6 +212,7 @@ extern "C" kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cac
   a.n = n;
   a.seq_len = seq_len;
   a.max_ctx = p.cfg.max_ctx;
+  a.key_excl = li.masks_current;
   a.batch = batch;
   a.causal = causal != 0;
   a.scale_log2 = scale_log2(p.cfg.head_dim);

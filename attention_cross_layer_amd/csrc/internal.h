@@ -67,6 +67,7 @@ struct DecodeLaunch {
   const void* q;
   const int32_t* seq_len;
   int32_t max_ctx;
+  int32_t key_excl;            // 1: the current position is masked (source above the layer)
   int32_t batch;
   int32_t n_splits;
   float scale_log2;            // log2(e) / sqrt(hd)
@@ -114,6 +115,7 @@ struct PrefillLaunch {
   int32_t n;
   const int32_t* seq_len;
   int32_t max_ctx;
+  int32_t key_excl;            // 1: the current position is masked (source above the layer)
   int32_t batch;
   int32_t causal;
   float scale_log2;
@@ -166,6 +168,7 @@ struct FactDecodeLaunch {
   const void* q;
   const int32_t* seq_len;
   int32_t max_ctx;
+  int32_t key_excl;            // 1: the current position is masked (source above the layer)
   int32_t batch;
   int32_t n_splits;
   float scale_log2;

@@ -71,6 +71,7 @@ struct DecodeParams {
   const char* q;
   const int32_t* seq_len;
   int32_t max_ctx;
+  int32_t key_excl;      // 1: keys 0..seq_len-2 only (source above the layer)
   int32_t n_splits;
   float scale_log2;
   float* ws_o;           // [B][Hq][S][HD]
@@ -229,7 +230,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams a) {
   // page: pass `way`, i.e. key 8*way + k8
   const int my_key = 8 * way + k8;
 
-  const int n_keys = clamp_len(a.seq_len[b], a.max_ctx);
+  const int n_keys = clamp_len(a.seq_len[b] - a.key_excl, a.max_ctx);
   const int n_pages = (n_keys + kPage - 1) / kPage;
   int pb, pe;
   split_range(n_pages, split, S, pb, pe);
@@ -526,6 +527,7 @@ int launch_decode(const DecodeLaunch& a, void* stream) {
   p.q = static_cast<const char*>(a.q);
   p.seq_len = a.seq_len;
   p.max_ctx = a.max_ctx;
+  p.key_excl = a.key_excl;
   p.n_splits = a.n_splits;
   p.scale_log2 = a.scale_log2;
   const size_t rows = (size_t)a.batch * a.n_q_heads * a.n_splits;

@@ -85,6 +85,7 @@ struct FactParams {
   const uint16_t* q;
   const int32_t* seq_len;
   int32_t max_ctx;
+  int32_t key_excl;     // 1: keys 0..seq_len-2 only (source above the layer)
   int32_t n_splits;
   float scale_log2;
   float* ws_c;          // [B][Hq][S][48]
@@ -227,7 +228,7 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int S = a.n_splits;
 
-  const int n_keys = min(max(a.seq_len[b], 0), a.max_ctx);
+  const int n_keys = min(max(a.seq_len[b] - a.key_excl, 0), a.max_ctx);
   const int n_pages = (n_keys + kPage - 1) / kPage;
   int pb, pe;
   split_range(n_pages, split, S, pb, pe);
@@ -750,6 +751,7 @@ int launch_fact_decode(const FactDecodeLaunch& a, void* stream) {
   p.q = static_cast<const uint16_t*>(a.q);
   p.seq_len = a.seq_len;
   p.max_ctx = a.max_ctx;
+  p.key_excl = a.key_excl;
   p.n_splits = a.n_splits;
   p.scale_log2 = a.scale_log2;
   const size_t rows = (size_t)a.batch * a.n_q_heads * a.n_splits;

@@ -68,6 +68,7 @@ struct PrefillParams {
   const int32_t* seq_len;
   int32_t max_ctx;
   int32_t causal;
+  int32_t key_excl;     // 1: query at P sees keys 0..P-1 (source above the layer)
   float scale_log2;
   void* out;            // [B][n][Hq][hd]
   int32_t out_bf16;
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
   const int T = min(max(a.seq_len[b], 0), a.max_ctx);
   const int wg_last_row = min(n, (pgrp + 1) * PB * kRows) - 1;
   int kend = T;
-  if (a.causal) kend = min(T, T - n + wg_last_row + 1);
+  if (a.causal) kend = min(T, T - n + wg_last_row + 1 - a.key_excl);
   kend = max(kend, 0);
   const int n_tiles = (kend + 63) / 64;
 
@@ -147,10 +148,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
   const int row = i0 + col;
   const bool row_ok = row < n;
   const int pos = T - n + row;                               // absolute position
-  const int row_kend = !row_ok ? 0 : (a.causal ? min(T, pos + 1) : T);
+  const int row_kend = !row_ok ? 0 : (a.causal ? max(min(T, pos + 1 - a.key_excl), 0) : T);
   // tiles below this one need no key mask in any row of the wave (the wave's
   // first row has the smallest key limit; rows past n make the wave masked)
-  const int wave_kend = (i0 + kRows <= n) ? (a.causal ? min(T, T - n + i0 + 1) : T) : 0;
+  const int wave_kend = (i0 + kRows <= n) ? (a.causal ? max(min(T, T - n + i0 + 1 - a.key_excl), 0) : T) : 0;
   const int unmasked_tiles = wave_kend / 64;
 
   uint4 qreg[KS];
@@ -395,6 +396,7 @@ int launch_prefill(const PrefillLaunch& a, void* stream) {
   p.seq_len = a.seq_len;
   p.max_ctx = a.max_ctx;
   p.causal = a.causal;
+  p.key_excl = a.key_excl;
   p.scale_log2 = a.scale_log2;
   p.out = a.out;
   p.out_bf16 = a.out_dtype == KVS_BF16;

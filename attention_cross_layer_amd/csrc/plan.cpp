@@ -8,8 +8,9 @@
 // Reconstruction", Abstract) reads a pair of stride-aligned sources; the
 // cross-layer sharing study ("A Systematic Study of Cross-Layer KV Sharing for
 // Efficient LLM Inference", TL;DR) distinguishes bottom configurations (sources
-// below the reader) from top/middle ones (sources above), which this build
-// rejects as unsupported.
+// below the reader) from top/middle ones (sources above, served with diagonal
+// masking: such a layer runs before its source has written the current
+// token, so its query skips the current position).
 #include <cmath>
 #include <cstring>
 #include <new>
@@ -79,9 +80,6 @@ extern "C" kvs_status kvs_share_plan(const kvs_config* cfg, const int32_t* src, 
       return fail(KVS_ERR_UNSUPPORTED, "factorized plans take one source per layer");
     if ((s0 == l || s1 == l) && !is_owner_row(src, w, l))
       return fail(KVS_ERR_MAP, "layer " + std::to_string(l) + ": a self-reference must be the plain owner row");
-    if (s0 > l || s1 > l)
-      return fail(KVS_ERR_UNSUPPORTED, "layer " + std::to_string(l) +
-                                           ": source above its reader (top/middle configuration)");
     if (!is_owner_row(src, w, s0) || (n == 2 && !is_owner_row(src, w, s1)))
       return fail(KVS_ERR_NOT_SOURCE, "layer " + std::to_string(l) + ": source owns no cache entries");
   }
@@ -107,6 +105,7 @@ extern "C" kvs_status kvs_share_plan(const kvs_config* cfg, const int32_t* src, 
       li.weight[j] = used ? (w ? w[2 * l + j] : 1.0f) : 0.0f;
     }
     if (li.n_src == 2) ++p.n_mixed;
+    li.masks_current = (li.src_layer[0] > l || li.src_layer[1] > l) ? 1 : 0;
   }
   if (p.n_mixed > 0 &&
       !decode_shape_supported(cfg->dtype, cfg->head_dim, cfg->n_q_heads / cfg->n_kv_heads, 2)) {

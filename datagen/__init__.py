@@ -61,7 +61,7 @@ class Workload:
     ctx: int                   # keys visible to the decode query (incl. itself)
     seed: int
     kind: str = "dense"        # "dense" or "factorized"
-    share: str = "cla2"        # "cla2", "depthgraft", "identity", "pairs"
+    share: str = "cla2"        # "cla2", "cla2_top", "mid3", "depthgraft", "identity", "pairs", "pairs_top"
     peaky_frac: float = 0.0    # fraction of keys whose vector is scaled by 4
     prefill_n: int = 0         # prefill chunk length (0: none)
     prefill_batch: int = 0
@@ -120,6 +120,16 @@ def share_map(wl: Workload, device="cpu") -> Tuple[torch.Tensor, torch.Tensor]:
     if wl.share in ("cla2", "pairs"):
         for l in range(L):
             src[l, 0] = 2 * (l // 2)
+            w[l, 0] = 1.0
+    elif wl.share in ("cla2_top", "pairs_top"):
+        # adjacent pairs whose upper layer holds the K/V (a top configuration)
+        for l in range(L):
+            src[l, 0] = min(2 * (l // 2) + 1, L - 1)
+            w[l, 0] = 1.0
+    elif wl.share == "mid3":
+        # groups of three layers served by the middle one (a middle configuration)
+        for l in range(L):
+            src[l, 0] = min(3 * (l // 3) + 1, L - 1)
             w[l, 0] = 1.0
     elif wl.share == "identity":
         for l in range(L):

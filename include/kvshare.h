@@ -96,6 +96,9 @@ typedef struct {
   int32_t src_layer[2];    /* source layers (-1 when unused)                    */
   int32_t src_slot[2];     /* their owner slots (-1 when unused)                */
   float   weight[2];       /* mixing weights as stored (fp32)                   */
+  int32_t masks_current;   /* 1: a source sits above the layer (top/middle
+                              configuration), so the layer's query sees only
+                              earlier positions (diagonal masking)           */
 } kvs_layer_info;
 
 typedef struct {
@@ -170,10 +173,14 @@ typedef struct {
  *   w    [n_layers][2] host float or NULL (NULL: all weights 1).
  * Rules (first violation wins, layers scanned in order): indices in range and
  * weights finite, else KVS_ERR_MAP; a row naming its own layer must be the
- * plain owner row, else KVS_ERR_MAP; a source above its reader ->
- * KVS_ERR_UNSUPPORTED (top/middle configurations); a source that owns no
- * entries -> KVS_ERR_NOT_SOURCE (reusing layers compute no K/V, CLA
- * Methodology, so chains are invalid).  KVS_FACTORIZED plans take single
+ * plain owner row, else KVS_ERR_MAP; a source that owns no entries ->
+ * KVS_ERR_NOT_SOURCE (reusing layers compute no K/V, CLA Methodology, so
+ * chains are invalid).  A source may sit above its reader (the top/middle
+ * configurations of "A Systematic Study of Cross-Layer KV Sharing for
+ * Efficient LLM Inference", TL;DR): that source writes the current token's
+ * entry only after the reader has run, so the reader's decode query sees
+ * positions 0..seq_len-2 and its causal prefill query at position P sees
+ * keys 0..P-1 (diagonal masking; a query with no key yields zeros).  KVS_FACTORIZED plans take single
  * sources only: src[l][0] is the layer that writes the pair's coefficients.
  * On success *out receives a plan to release with kvs_plan_free(). */
 KVS_API kvs_status kvs_share_plan(const kvs_config* cfg, const int32_t* src,

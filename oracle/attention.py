@@ -71,12 +71,14 @@ def effective_kv(src_row, w_row, owner_k: dict, owner_v: dict):
     return k, v
 
 
-def attend_decode(q, k, v, seq_len, scale=None):
+def attend_decode(q, k, v, seq_len, scale=None, exclude_current=False):
     """One query per (sequence, head) over keys 0..seq_len[b]-1.
 
     q [B, Hq, hd]; k, v [B, T, Hkv, hd]; returns float64 [B, Hq, hd].
     out[b, h] = sum_t softmax_t(scale * q[b,h] . k[b,t,g]) v[b,t,g],
-    g = h // (Hq / Hkv), scale = 1/sqrt(hd) unless given.
+    g = h // (Hq / Hkv), scale = 1/sqrt(hd) unless given.  With
+    ``exclude_current`` the query (at position seq_len[b]-1) sees keys
+    0..seq_len[b]-2 only (diagonal masking); no key at all gives zeros.
     """
     q = f64(q)
     k = f64(k)
@@ -88,7 +90,7 @@ def attend_decode(q, k, v, seq_len, scale=None):
         scale = 1.0 / np.sqrt(hd)
     out = np.zeros((B, Hq, hd), dtype=np.float64)
     for b in range(B):
-        T = int(seq_len[b])
+        T = int(seq_len[b]) - (1 if exclude_current else 0)
         if T <= 0:
             continue
         for h in range(Hq):
@@ -100,13 +102,15 @@ def attend_decode(q, k, v, seq_len, scale=None):
     return out
 
 
-def attend_prefill(q, k, v, seq_len, causal=True, scale=None):
+def attend_prefill(q, k, v, seq_len, causal=True, scale=None, exclude_current=False):
     """A chunk of n queries per sequence, the last n positions of the sequence.
 
     q [B, n, Hq, hd]; k, v [B, T, Hkv, hd] hold keys 0..seq_len[b]-1 (the chunk's
     own keys included).  Query i sits at absolute position
     P_i = seq_len[b] - n + i; with ``causal`` it sees keys 0..P_i (inclusive
-    diagonal), otherwise keys 0..seq_len[b]-1.  Returns float64 [B, n, Hq, hd].
+    diagonal), or keys 0..P_i - 1 with ``exclude_current`` (diagonal masking),
+    otherwise keys 0..seq_len[b]-1.  A query that sees no key gets zeros.
+    Returns float64 [B, n, Hq, hd].
     """
     q = f64(q)
     k = f64(k)
@@ -124,11 +128,15 @@ def attend_prefill(q, k, v, seq_len, causal=True, scale=None):
             z = scale * (q[b, :, h, :] @ k[b, :T, g, :].T)          # [n, T]
             if causal:
                 pos = T - n + np.arange(n)
-                visible = np.arange(T)[None, :] <= pos[:, None]
+                last = pos - (1 if exclude_current else 0)
+                visible = np.arange(T)[None, :] <= last[:, None]
                 z = np.where(visible, z, -np.inf)
-            z = z - z.max(axis=1, keepdims=True)
-            e = np.exp(z)
-            out[b, :, h, :] = (e @ v[b, :T, g, :]) / e.sum(axis=1, keepdims=True)
+            for i in range(n):
+                if not np.isfinite(z[i]).any():
+                    continue                      # no visible key: zeros
+                zi = z[i] - z[i].max()
+                e = np.exp(zi)
+                out[b, i, h, :] = (e @ v[b, :T, g, :]) / e.sum()
     return out
 
 
@@ -158,14 +166,23 @@ def factorized_kv(c, basis, scale, d, u, rank):
     return base + scale[..., None] * resid
 
 
+def _reads_above(src, layer):
+    """A source above the reader (top/middle configuration, "A Systematic
+    Study of Cross-Layer KV Sharing for Efficient LLM Inference", TL;DR:
+    diagonal masking): its K/V for the current token does not exist yet."""
+    return any(int(s) > layer for s in src[layer] if int(s) >= 0)
+
+
 def layer_decode(src, w, layer, owner_k, owner_v, q, seq_len):
     """Decode output of ``layer`` under map (src, w): effective K/V, then
-    attention.  Returns float64 [B, Hq, hd]."""
+    attention; a layer reading a source above it skips the current position.
+    Returns float64 [B, Hq, hd]."""
     k, v = effective_kv(src[layer], w[layer], owner_k, owner_v)
-    return attend_decode(q, k, v, seq_len)
+    return attend_decode(q, k, v, seq_len, exclude_current=_reads_above(src, layer))
 
 
 def layer_prefill(src, w, layer, owner_k, owner_v, q, seq_len, causal=True):
     """Prefill-chunk output of ``layer`` under map (src, w)."""
     k, v = effective_kv(src[layer], w[layer], owner_k, owner_v)
-    return attend_prefill(q, k, v, seq_len, causal=causal)
+    return attend_prefill(q, k, v, seq_len, causal=causal,
+                          exclude_current=_reads_above(src, layer))

@@ -12,9 +12,12 @@ What the pages fix:
 * DepthGraft page, Abstract: deep-layer K/V is rebuilt from stride-aligned
   shallow/middle source pairs and the cache shrinks by roughly one third.
 * "A Systematic Study of Cross-Layer KV Sharing for Efficient LLM
-  Inference", TL;DR: the bottom configurations take K/V from lower layers;
-  the top/middle ones pair queries with K/V of upper layers.  Only maps with
-  every source at or below its reader are in scope here.
+  Inference", TL;DR and Abstract: the bottom configurations take K/V from
+  lower layers; the top/middle ones pair queries with K/V of upper layers,
+  and inference with them relies on diagonal masking.  Reading: when a
+  layer runs, a source above it has not yet produced the current token's
+  K/V, so such a layer's query sees only earlier positions (the diagonal of
+  its causal mask is removed); see ``excludes_current``.
 
 Map encoding: ``src`` [L, 2] ints (-1 = unused second entry), ``w`` [L, 2]
 float weights.  A layer owns its K/V iff its row is ((l, 1.0), (-1, *)).
@@ -26,7 +29,7 @@ import math
 OK = "ok"
 ERR_MAP = "map"                 # malformed row: bad index, weight, or self-row shape
 ERR_NOT_SOURCE = "not_source"   # a source that does not own K/V (a chain)
-ERR_UNSUPPORTED = "unsupported"  # a source above its reader (top/middle family)
+ERR_UNSUPPORTED = "unsupported"  # more sources than a factorized plan takes
 
 
 def owns(src, w, l) -> bool:
@@ -36,9 +39,10 @@ def owns(src, w, l) -> bool:
 def check(src, w, max_sources_factorized=None) -> str:
     """Classify a map: OK or the first violated rule, scanning layers in order
     and, within a layer, the rules in the order: index range and weight
-    finiteness (ERR_MAP), a self-reference that is not the plain owner row
-    (ERR_MAP), source above the reader (ERR_UNSUPPORTED), source that does not
-    own K/V (ERR_NOT_SOURCE)."""
+    finiteness (ERR_MAP), more than one source in a factorized plan
+    (ERR_UNSUPPORTED), a self-reference that is not the plain owner row
+    (ERR_MAP), a source that does not own K/V (ERR_NOT_SOURCE).  Sources above
+    their reader (top/middle configurations) are allowed."""
     L = len(src)
     if L == 0:
         return ERR_MAP
@@ -56,9 +60,6 @@ def check(src, w, max_sources_factorized=None) -> str:
             return ERR_UNSUPPORTED
         if l in row[:n] and not owns(src, w, l):
             return ERR_MAP
-        for j in range(n):
-            if row[j] > l:
-                return ERR_UNSUPPORTED
         for j in range(n):
             if not owns(src, w, row[j]):
                 return ERR_NOT_SOURCE
@@ -83,6 +84,13 @@ def layer_sources(src, w, l):
         if s >= 0:
             out.append((s, sl[s], float(w[l][j])))
     return out
+
+
+def excludes_current(src, w, l) -> bool:
+    """Whether layer l reads a source above it (a top/middle configuration):
+    that source writes the current token's K/V only after layer l has run,
+    so layer l's query attends to earlier positions only."""
+    return any(int(s) > l for s in src[l] if int(s) >= 0)
 
 
 def last_owner_layer(src, w) -> int:

@@ -11,6 +11,7 @@ import torch
 import attention_cross_layer_amd as K
 import datagen
 from oracle import attention as A
+from oracle import plan as P
 
 TOL_ABS = 1e-2     # max-abs error bound for bf16 inputs with fp32 accumulation
 TOL_REL = 5e-3     # relative L2 error bound
@@ -177,4 +178,5 @@ class Factorized:
     def oracle_decode(self, layer, q=None):
         q = self.q(layer) if q is None else q
         k, v = self.kv(layer)
-        return A.attend_decode(q, k, v, self.lens.tolist())
+        return A.attend_decode(q, k, v, self.lens.tolist(),
+                               exclude_current=P.excludes_current(self.src.tolist(), self.w.tolist(), layer))

@@ -63,6 +63,7 @@ def _assert_plan_matches_oracle(plan, src, w):
             assert li.weight[j] == float(torch.tensor(s_w, dtype=torch.float32))
         for j in range(len(want), 2):
             assert li.src_layer[j] == -1 and li.src_slot[j] == -1
+        assert li.masks_current == int(P.excludes_current(src, w, l))
 
 
 @pytest.mark.parametrize("name", ["tiny_cla2", "tinyllama_cla2", "depthgraft", "cla2_64k"])

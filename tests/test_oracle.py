@@ -410,12 +410,71 @@ def test_plan_slot_numbering_ascending():
     ([[0, -1], [2, -1]], [[1.0, 0], [1.0, 0]], P.ERR_MAP),          # out of range
     ([[0, -1], [1, -1], [1, -1]], [[1.0, 0], [0.5, 0], [1.0, 0]], P.ERR_MAP),  # self row w != 1
     ([[0, -1], [0, -1], [1, -1]], [[1.0, 0]] * 3, P.ERR_NOT_SOURCE),  # chain
-    ([[1, -1], [1, -1]], [[1.0, 0], [1.0, 0]], P.ERR_UNSUPPORTED),  # source above reader
+    ([[1, -1], [1, -1]], [[1.0, 0], [1.0, 0]], P.OK),               # source above reader (top)
+    ([[1, -1], [1, -1], [1, -1]], [[1.0, 0]] * 3, P.OK),             # middle: 0 and 2 read 1
+    ([[2, -1], [2, -1], [1, -1]], [[1.0, 0]] * 3, P.ERR_NOT_SOURCE), # 2 reads a non-owner
     ([[0, -1], [0, -1]], [[1.0, 0], [float("nan"), 0]], P.ERR_MAP),
     ([[0, -1], [1, 0]], [[1.0, 0], [0.5, 0.5]], P.ERR_MAP),           # self + other
 ])
 def test_plan_rules(src, w, want):
     assert P.check(src, w) == want
+
+
+# ----------------------------------------------------------------------------
+# top / middle configurations: diagonal masking ("A Systematic Study of
+# Cross-Layer KV Sharing for Efficient LLM Inference", TL;DR)
+# ----------------------------------------------------------------------------
+
+def check_strict_prefill(attend_prefill=A.attend_prefill):
+    """Strict causal prefill (query at P sees keys j < P) against the library
+    SDPA with the explicit strict mask, at offset 0 (first row: no key,
+    zeros) and at offset 12."""
+    B, n, Hq, Hkv, hd, T = 2, 7, 4, 2, 16, 19
+    q = _rand((B, n, Hq, hd), 61)
+    k = _rand((B, T, Hkv, hd), 62)
+    v = _rand((B, T, Hkv, hd), 63)
+    err = 0.0
+    mask = torch.ones(n, T, dtype=torch.bool).tril(diagonal=T - n - 1)
+    out = attend_prefill(q.numpy(), k.numpy(), v.numpy(), [T, T], causal=True, exclude_current=True)
+    err = max(err, float(np.max(np.abs(out - _sdpa(q, k, v, Hq // Hkv, mask=mask).numpy()))))
+    mask0 = torch.ones(n, n, dtype=torch.bool).tril(diagonal=-1)
+    out0 = attend_prefill(q.numpy(), k[:, :n].numpy(), v[:, :n].numpy(), [n, n], causal=True,
+                          exclude_current=True)
+    ref0 = _sdpa(q[:, 1:], k[:, :n], v[:, :n], Hq // Hkv, mask=mask0[1:]).numpy()
+    err = max(err, float(np.max(np.abs(out0[:, 1:] - ref0))))
+    err = max(err, float(np.max(np.abs(out0[:, 0]))))            # position 0 sees nothing
+    return err
+
+
+def test_strict_prefill_matches_sdpa_with_strict_mask():
+    assert check_strict_prefill() < 1e-12
+
+
+def test_top_decode_skips_the_current_position():
+    """A layer reading a source above it: at seq_len T its query equals a
+    plain decode over keys 0..T-2 (a different routine: attend over an
+    explicitly shortened cache), and T = 1 gives zeros."""
+    B, Hq, Hkv, hd, T = 2, 4, 2, 16, 9
+    q = _rand((B, Hq, hd), 71)
+    k = _rand((B, T, Hkv, hd), 72)
+    v = _rand((B, T, Hkv, hd), 73)
+    src = [[1, -1], [1, -1]]
+    w = [[1.0, 0.0], [1.0, 0.0]]
+    top = A.layer_decode(src, w, 0, {1: k.numpy()}, {1: v.numpy()}, q.numpy(), [T, T])
+    ref = _sdpa(q[:, None], k[:, :T - 1], v[:, :T - 1], Hq // Hkv)[:, 0].numpy()
+    assert np.max(np.abs(top - ref)) < 1e-12
+    own = A.layer_decode(src, w, 1, {1: k.numpy()}, {1: v.numpy()}, q.numpy(), [T, T])
+    assert np.max(np.abs(own - _sdpa(q[:, None], k, v, Hq // Hkv)[:, 0].numpy())) < 1e-12
+    assert np.all(A.layer_decode(src, w, 0, {1: k.numpy()}, {1: v.numpy()}, q.numpy(), [1, 1]) == 0)
+    assert P.excludes_current(src, w, 0) and not P.excludes_current(src, w, 1)
+
+
+def test_top_cla2_halves_the_cache():
+    src = [[1, -1], [1, -1], [3, -1], [3, -1]]
+    w = [[1.0, 0.0]] * 4
+    assert P.check(src, w) == P.OK
+    assert P.cache_fraction(src, w) == 0.5
+    assert [P.excludes_current(src, w, l) for l in range(4)] == [True, False, True, False]
 
 
 # ----------------------------------------------------------------------------
@@ -445,6 +504,11 @@ def test_planted_mistakes_are_caught(golden_dir, monkeypatch):
         return out
 
     assert check_causal(cau, strict_causal) > 0.1
+
+    def inclusive_diagonal(q, k, v, seq_len, causal=True, scale=None, exclude_current=False):
+        return A.attend_prefill(q, k, v, seq_len, causal=causal)    # masking ignored
+
+    assert check_strict_prefill(inclusive_diagonal) > 0.1
 
     def rank_off_by_one(c, basis, scale, d, u, rank):
         return A.factorized_kv(c, basis, scale, d, u, np.asarray(rank) + 1)
