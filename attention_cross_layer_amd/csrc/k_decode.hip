@@ -458,8 +458,265 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams a) {
   }
 }
 
+// ---------------------------------------------------------------- MFMA path
+// bf16, hd 64, one source, G <= 16: both products of a page on
+// v_mfma_f32_16x16x32_bf16 (A: lane l holds row l%16, k = 8(l/16)..+7;
+// B: column l%16, same k; result register r of lane l is row 4(l/16)+r,
+// column l%16), reading the cache in its stored layouts:
+//   scores  S[keys][heads] = K q^T: A = 16 keys x 32 dims, one 16-byte load of
+//           a K row per lane; B = the G queries (columns >= G zero), in
+//           registers for the whole launch.  Lane (g = l/16, h = l%16) ends
+//           with keys 16kb + 4g + r (kb = 0..3, r = 0..3) of head h.
+//   values  O[heads][dims] = P^T V over 32 keys per step, the keys of step ps
+//           taken in the order those registers hold them:
+//           k = 8g + e  ->  key 32ps + 16(e/4) + 4g + e%4,
+//           so P^T is the lane's own (bf16) probabilities and the matching V
+//           operand is 4 dwords of the pair-interleaved V page (each dword =
+//           one dim of two consecutive keys).
+// The online softmax keeps one running maximum per head (raw scores; the
+// positive scale is applied inside the exponent), so only heads whose
+// maximum moved rescale their accumulators.
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_pk_t;
+
+__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+  const bf16x2_pk_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// max over the 4 rows of 16 lanes (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float row_max4(float x) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+struct MfmaPage {
+  uint4 k[4][2];      // [kb][ks]: key 16kb + l%16, dims 8(l/16) + 32ks .. +7
+  uint4 v[2][4];      // [ps][db]: 4 dwords (pairs) of dim 16db + l%16
+};
+
+template <int G>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams a) {
+  constexpr int HD = 64;
+  static_assert(G <= 16, "one 16-column block of heads");
+  __shared__ float mrg_o[4][G][HD];
+  __shared__ float mrg_m[4][G];
+  __shared__ float mrg_l[4][G];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int S = a.n_splits;
+  const int col = lane & 15, g = lane >> 4;
+
+  // B operand of the scores: head `col`, dims 8g + 32ks .. +7
+  uint4 qf[2];
+  {
+    const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((size_t)b * a.n_q_heads + (size_t)kvh * G + (col < G ? col : 0)) * HD;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint4 x = *reinterpret_cast<const uint4*>(qh + 8 * g + 32 * ks);
+      qf[ks] = col < G ? x : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  const int n_keys = clamp_len(a.seq_len[b] - a.key_excl, a.max_ctx);
+  const int n_pages = (n_keys + kPage - 1) / kPage;
+  int pb, pe;
+  split_range(n_pages, split, S, pb, pe);
+  const int32_t* pt = a.page_table + (size_t)b * a.pages_per_seq;
+  const uint16_t* kbase = reinterpret_cast<const uint16_t*>(a.k_pool) + (int64_t)a.slot0 * a.slot_stride;
+  const uint16_t* vbase = reinterpret_cast<const uint16_t*>(a.v_pool) + (int64_t)a.slot0 * a.slot_stride;
+
+  auto next_page = [&](int from) {
+    int p = from;
+    while (p < pe && (unsigned)pt[p] >= (unsigned)a.n_phys_pages) p += 4;
+    return p;
+  };
+  auto load = [&](int pg, MfmaPage& r) {
+    const int64_t tile = ((int64_t)pt[pg] * a.n_kv_heads + kvh) * (kPage * HD);
+    const uint16_t* kt = kbase + tile;
+    const uint32_t* vt = reinterpret_cast<const uint32_t*>(vbase + tile);   // [32 pairs][64 dims]
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        r.k[kb][ks] = *reinterpret_cast<const uint4*>(kt + (16 * kb + col) * HD + 8 * g + 32 * ks);
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const int d = 16 * db + col;
+        const int p0 = 16 * ps + 2 * g, p1 = p0 + 8;           // pairs of keys 32ps+4g.., 32ps+16+4g..
+        r.v[ps][db] = make_uint4(vt[p0 * HD + d], vt[(p0 + 1) * HD + d], vt[p1 * HD + d],
+                                 vt[(p1 + 1) * HD + d]);
+      }
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;   // for head `col`, over this lane's keys
+  f32x4_t o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint32_t ones = 0x3F803F80u;       // (1.0, 1.0) in bf16
+
+  auto compute = [&](int pg, MfmaPage& r) {
+    const int nvalid = n_keys - pg * kPage;
+    f32x4_t s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = mfma16(r.k[kb][0], qf[0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+      s[kb] = mfma16(r.k[kb][1], qf[1], s[kb]);
+    }
+    if (nvalid < kPage || G < 16) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[kb][e] = (col < G && 16 * kb + 4 * g + e < nvalid) ? s[kb][e] : -INFINITY;
+    }
+    float mt = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+    for (int kb = 1; kb < 4; ++kb) mt = fmaxf(mt, fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3])));
+    mt = row_max4(mt);
+    const float mn = fmaxf(m_run, mt);
+    const float neg = mn == -INFINITY ? 0.f : -mn * a.scale_log2;
+    const float alpha = m_run == mn ? 1.f : dev::fast_exp2(fmaf(m_run, a.scale_log2, neg));
+    m_run = mn;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+      // accumulator entry rr of lane l belongs to head 4(l/16) + rr
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const float f = __shfl(alpha, 4 * g + rr);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db][rr] *= f;
+      }
+      l_run *= alpha;
+    }
+    uint4 pf[2];
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps) {
+      const f32x4_t& s0 = s[2 * ps];
+      const f32x4_t& s1 = s[2 * ps + 1];
+      pf[ps].x = pack_bf16_rne(dev::fast_exp2(fmaf(s0[0], a.scale_log2, neg)), dev::fast_exp2(fmaf(s0[1], a.scale_log2, neg)));
+      pf[ps].y = pack_bf16_rne(dev::fast_exp2(fmaf(s0[2], a.scale_log2, neg)), dev::fast_exp2(fmaf(s0[3], a.scale_log2, neg)));
+      pf[ps].z = pack_bf16_rne(dev::fast_exp2(fmaf(s1[0], a.scale_log2, neg)), dev::fast_exp2(fmaf(s1[1], a.scale_log2, neg)));
+      pf[ps].w = pack_bf16_rne(dev::fast_exp2(fmaf(s1[2], a.scale_log2, neg)), dev::fast_exp2(fmaf(s1[3], a.scale_log2, neg)));
+      // the running sum adds the same bf16-rounded probabilities
+      l_run = dot2_bf16(pf[ps].x, ones, l_run);
+      l_run = dot2_bf16(pf[ps].y, ones, l_run);
+      l_run = dot2_bf16(pf[ps].z, ones, l_run);
+      l_run = dot2_bf16(pf[ps].w, ones, l_run);
+    }
+    if (nvalid < kPage) {
+      // keys past the sequence end: p = 0, but unwritten V memory may hold NaN
+      // patterns and 0 * NaN is NaN
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps) {
+        const int k0 = 32 * ps + 4 * g, k1 = k0 + 16;
+        const uint32_t m0 = (k0 < nvalid ? 0x0000ffffu : 0u) | (k0 + 1 < nvalid ? 0xffff0000u : 0u);
+        const uint32_t m1 = (k0 + 2 < nvalid ? 0x0000ffffu : 0u) | (k0 + 3 < nvalid ? 0xffff0000u : 0u);
+        const uint32_t m2 = (k1 < nvalid ? 0x0000ffffu : 0u) | (k1 + 1 < nvalid ? 0xffff0000u : 0u);
+        const uint32_t m3 = (k1 + 2 < nvalid ? 0x0000ffffu : 0u) | (k1 + 3 < nvalid ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          r.v[ps][db].x &= m0;
+          r.v[ps][db].y &= m1;
+          r.v[ps][db].z &= m2;
+          r.v[ps][db].w &= m3;
+        }
+      }
+    }
+#pragma unroll
+    for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[db] = mfma16(pf[ps], r.v[ps][db], o[db]);
+  };
+
+  // two page buffers: the next page's loads are in flight during a compute
+  MfmaPage bufA, bufB;
+  int pg = next_page(pb + wave);
+  if (pg < pe) load(pg, bufA);
+  while (pg < pe) {
+    const int pn = next_page(pg + 4);
+    if (pn < pe) load(pn, bufB);
+    compute(pg, bufA);
+    if (pn >= pe) break;
+    const int pn2 = next_page(pn + 4);
+    if (pn2 < pe) load(pn2, bufA);
+    compute(pn, bufB);
+    pg = pn2;
+  }
+
+  // ---- this wave's (O, m, l) to LDS; m in log2 units as the merge expects
+  {
+    float l = l_run;
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (g == 0 && col < G) {
+      mrg_m[wave][col] = m_run == -INFINITY ? -INFINITY : m_run * a.scale_log2;
+      mrg_l[wave][col] = l;
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int h = 4 * g + rr;
+        if (h < G) mrg_o[wave][h][16 * db + col] = o[db][rr];
+      }
+  }
+  __syncthreads();
+
+  const size_t hq0 = (size_t)b * a.n_q_heads + (size_t)kvh * G;
+  for (int e = tid; e < G * HD; e += 256) {
+    const int h = e / HD, d = e % HD;
+    float M = mrg_m[0][h];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, mrg_m[w][h]);
+    float ov = 0.f, l = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = dev::fast_exp2(mrg_m[w][h] - M);
+        ov = fmaf(f, mrg_o[w][h][d], ov);
+        l = fmaf(f, mrg_l[w][h], l);
+      }
+    }
+    if (S == 1) {
+      store_out(a.out, (hq0 + h) * HD + d, l > 0.f ? ov / l : 0.f, a.out_bf16);
+    } else {
+      const size_t row = (hq0 + h) * S + split;
+      a.ws_o[row * HD + d] = ov;
+      if (d == 0) {
+        a.ws_m[row] = M;
+        a.ws_l[row] = l;
+      }
+    }
+  }
+}
+
+template <int G>
+int run_decode_mfma(const DecodeParams& p, int B, hipStream_t st) {
+  dim3 grid(p.n_splits, p.n_kv_heads, B);
+  hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(256), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_splits == 1) return (int)e;
+  hipLaunchKernelGGL((decode_merge_kernel<G, 64>), dim3(p.n_kv_heads, B), dim3(256), 0, st, p);
+  return (int)hipGetLastError();
+}
+
 template <typename T, int HD, int G, int NSRC>
 int run_decode(const DecodeParams& p, int B, hipStream_t st) {
+  if constexpr (sizeof(T) == 2 && HD == 64 && NSRC == 1 && G <= 16) return run_decode_mfma<G>(p, B, st);
   dim3 grid(p.n_splits, p.n_kv_heads, B);
   hipLaunchKernelGGL((decode_kernel<T, HD, G, NSRC>), grid, dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
