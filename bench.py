@@ -145,9 +145,11 @@ def cpu_baseline(wl, src, w, host_seq, budget_s=12.0):
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+PREFILL_WORKLOAD = "depthgraft_prefill_chunk"
 CALIB_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {"decode_kernel": "k_decode.hip", "fact_decode_kernel": "k_factorized.hip",
+KERNEL_SOURCES = {"decode_kernel": "k_decode.hip", "decode_mfma_kernel": "k_decode.hip",
+                  "fact_decode_kernel": "k_factorized.hip",
                   "prefill_kernel": "k_prefill.hip"}
 
 
@@ -221,7 +223,13 @@ def algorithmic_bytes(wl, kernel):
         sum_r = B * (16 * n_hi + 8 * ((T - n_hi) // 2))   # exact per-rank token counts
         tokens = B * T
         return wl.n_kv_heads * (tokens * (2 * wl.basis_rank * 2 + 4) + 2 * sum_r) + tokens
-    nsrc = int(kernel.rstrip(">").split(",")[-1]) if "<" in kernel else 1
+    if kernel.startswith("prefill_kernel"):
+        # queries in, outputs out (bf16), every K/V tile of the sequence once
+        n, T = wl.prefill_n, wl.ctx
+        return (n * wl.n_q_heads * wl.head_dim * 2 * 2
+                + wl.batch * T * wl.n_kv_heads * wl.head_dim * 2 * 2)
+    nsrc = (int(kernel.rstrip(">").split(",")[-1])
+            if "<" in kernel and kernel.startswith("decode_kernel") else 1)
     elem = 4 if wl.dtype == "f32" else 2
     return wl.batch * wl.n_kv_heads * wl.ctx * wl.head_dim * 2 * elem * nsrc
 
@@ -232,14 +240,16 @@ def record_profile(prof_dir, kernel, workload, s):
     import csv
     import glob
 
-    wl = datagen.WORKLOADS[workload]
+    prefill = workload == PREFILL_WORKLOAD
+    wl = datagen.WORKLOADS["depthgraft"].with_(batch=1) if prefill else datagen.WORKLOADS[workload]
     base = kernel.split("<")[0]
     f = glob.glob(os.path.join(prof_dir, "kt", "*kernel_stats.csv"))
     allk = sorted(csv.DictReader(open(f[0])), key=lambda r: -float(r["TotalDurationNs"]))
     top = [r for r in allk if "kvs::" in r["Name"]] + [r for r in allk if "kvs::" not in r["Name"]][:4]
     alg = algorithmic_bytes(wl, kernel)
     fetch, write = s["FETCH_SIZE"]["bytes_per_dispatch"], s["WRITE_SIZE"]["bytes_per_dispatch"]
-    cmd = f"python3 bench.py --workload {workload} --roofline-only"
+    cmd = ("python3 bench.py --prefill --steps 2 --warmup 1" if prefill
+           else f"python3 bench.py --workload {workload} --roofline-only")
     lines = [
         f"# `{kernel}` on `{workload}`", "",
         "Commands (from the repository root, profile directory `P`):", "", "```",
@@ -279,6 +289,26 @@ def record_profile(prof_dir, kernel, workload, s):
                      "profile": os.path.relpath(out, ROOT)}
     json.dump(rec, open(TRAFFIC_FILE, "w"), indent=1, sort_keys=True)
     return out
+
+
+def calibration_copy():
+    """Reference copy of known size for calibrating the HBM byte counters of a
+    profiled run: 256 MiB read + 256 MiB written by PyTorch's elementwise
+    copy kernel, cache flushed first (the run's last device copy)."""
+    flush = torch.ones((FLUSH_BYTES // 4 // 4096, 4096), dtype=torch.float32, device="cuda")
+    ref_src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    ref_dst = torch.empty_like(ref_src)
+    flush.sum(dim=0)
+    ref_dst.copy_(ref_src)
+    torch.cuda.synchronize()
+
+
+def decode_kernel_name(wl, two_source):
+    """The kernel a decode call of this workload launches for its partitions."""
+    G = wl.n_q_heads // wl.n_kv_heads
+    if wl.dtype == "bf16" and wl.head_dim == 64 and not two_source and G <= 16:
+        return "decode_mfma_kernel (bf16 MFMA, split-K partitions)"
+    return "decode_kernel (split-K partitions)"
 
 
 def prefill_flops(n, T, n_q_heads, hd):
@@ -342,7 +372,7 @@ def prefill_main(args):
            "value": n * 1000.0 / ms, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": "depthgraft_prefill_chunk", "owner_layers": len(owners),
+           "config": {"workload": PREFILL_WORKLOAD, "owner_layers": len(owners),
                       "batch": 1, "chunk": n, "ctx": T, "causal": True,
                       "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads,
                       "head_dim": wl.head_dim},
@@ -350,6 +380,11 @@ def prefill_main(args):
                         "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                         "traffic": None, "kernel": "prefill_kernel (bf16 MFMA, causal)",
                         "flops_per_launch": flops, "avg_launch_us": us}}
+    calibration_copy()
+    traffic = recorded_traffic(PREFILL_WORKLOAD)
+    if traffic is not None:
+        res["roofline"]["traffic"] = traffic["bytes_per_launch"]
+        res["roofline"]["traffic_source"] = traffic["source"]
     print(json.dumps(res), flush=True)
 
 
@@ -360,7 +395,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tinyllama_cla2",
                     choices=["tiny_cla2", "tinyllama_cla2", "depthgraft", "cla2_64k",
-                             "factorized_64k"])
+                             "factorized_64k", "tinyllama_cla2_top", PREFILL_WORKLOAD])
     ap.add_argument("--roofline-passes", type=int, default=3)
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the cache-flushed per-launch timing loop (for profiling)")
@@ -383,7 +418,7 @@ def main():
         if args.record:
             print(record_profile(args.summarize, args.kernel, args.workload, s))
         return
-    if args.prefill:
+    if args.prefill or args.workload == PREFILL_WORKLOAD:
         return prefill_main(args)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path is a "
@@ -494,7 +529,7 @@ def main():
                        "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                        "kernel": ("fact_decode_kernel (factorized cache, split-K partitions)"
                                   if fact else
-                                  "decode_kernel (split-K partitions), "
+                                  decode_kernel_name(wl, not single) + ", "
                                   + ("single-source layer" if single else "two-source layer")),
                        "bytes_per_launch": nbytes, "avg_launch_us": us,
                        "launches": sum(len(timed[l]) for l in dom), "cache": "flushed"}
@@ -504,15 +539,8 @@ def main():
         res["roofline_two_source"] = {"achieved": b2 / (us2 * 1e-6) / 1e9,
                                       "frac": b2 / (us2 * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                       "bytes_per_launch": b2, "avg_launch_us": us2}
-    # ---- reference copy of known size for calibrating the HBM byte
-    # counters of a profiled run: 256 MiB read + 256 MiB written by
-    # PyTorch's elementwise copy kernel, cache flushed first
-    ref_src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda")
-    ref_dst = torch.empty_like(ref_src)
-    flush.sum(dim=0)
-    ref_dst.copy_(ref_src)
-    torch.cuda.synchronize()
-    del flush, ref_src, ref_dst
+    del flush
+    calibration_copy()
     traffic = recorded_traffic(wl.name)
     if traffic is not None:
         res["roofline"]["traffic"] = traffic["bytes_per_launch"]

@@ -93,6 +93,10 @@ WORKLOADS = {
     "factorized_64k": Workload("factorized_64k", 32, 32, 8, 128, "bf16", 2, 65536,
                                0x5EED0 + 5, kind="factorized", share="pairs",
                                basis_rank=32, resid_rank_max=16, rank16_frac=0.1),
+    # the 1.1B shape with each adjacent pair served by its upper layer (a top
+    # configuration of the systematic cross-layer KV sharing study)
+    "tinyllama_cla2_top": Workload("tinyllama_cla2_top", 22, 32, 4, 64, "bf16", 64, 2048,
+                                   0x5EED0 + 6, share="cla2_top"),
 }
 
 
