@@ -268,8 +268,12 @@ def record_profile(prof_dir, kernel, workload, s):
         f"({fetch / alg:.3f} x algorithmic)",
         f"- WRITE_SIZE: {s['WRITE_SIZE']['kib_per_dispatch']:.1f} KiB/dispatch x "
         f"{s['WRITE_SIZE']['scale']:.4f} = {write:,.0f} B",
-        f"- algorithmic rate at the traced average: {alg / (s['avg_us'] * 1e-6) / 1e9:,.0f} GB/s "
-        f"({alg / (s['avg_us'] * 1e-6) / 1e9 / HBM_PEAK_GBS:.1%} of 8 TB/s)", "",
+        (f"- MFMA rate at the traced average: "
+         f"{prefill_flops(wl.prefill_n, wl.ctx, wl.n_q_heads, wl.head_dim) / (s['avg_us'] * 1e-6) / 1e12:,.0f}"
+         f" TFLOP/s ({prefill_flops(wl.prefill_n, wl.ctx, wl.n_q_heads, wl.head_dim) / (s['avg_us'] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS:.1%}"
+         f" of 2.5 PFLOP/s bf16; the profiler slows this launch)" if prefill else
+         f"- algorithmic rate at the traced average: {alg / (s['avg_us'] * 1e-6) / 1e9:,.0f} GB/s "
+         f"({alg / (s['avg_us'] * 1e-6) / 1e9 / HBM_PEAK_GBS:.1%} of 8 TB/s)"), "",
         "## Kernels of the traced run: this library's, then the largest others (set-up, "
         "and the 512 MB read that flushes the cache before each timed launch)", "",
         "| kernel | calls | avg us | share |", "|---|---:|---:|---:|"]
