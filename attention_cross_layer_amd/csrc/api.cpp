@@ -183,16 +183,61 @@ extern "C" kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cac
   if ((st = check_batch(plan, batch)) != KVS_OK) return st;
   if (n < 1 || n > p.cfg.max_ctx) return fail(KVS_ERR_RANGE, "n out of range");
   if (out_dtype != KVS_F32 && out_dtype != KVS_BF16) return fail(KVS_ERR_ARG, "bad out_dtype");
-  if (p.cfg.kind != KVS_DENSE || p.cfg.dtype != KVS_BF16)
-    return fail(KVS_ERR_UNSUPPORTED, "prefill runs on dense bf16 caches (bf16 MFMA)");
   const int32_t group = p.cfg.n_q_heads / p.cfg.n_kv_heads;
+  const kvs_layer_info& li = p.layers[layer];
+  if (p.cfg.kind == KVS_FACTORIZED) {
+    if (!fact_prefill_shape_supported(p.cfg.head_dim, group, p.cfg.basis_rank, p.cfg.resid_rank_max))
+      return fail(KVS_ERR_UNSUPPORTED, "no factorized prefill kernel for this shape");
+    if (!cache->ck_pool || !cache->cv_pool || !cache->dk_pool || !cache->dv_pool || !cache->sk_pool ||
+        !cache->sv_pool || !cache->rank_pool || !cache->page_table || !cache->basis_k ||
+        !cache->basis_v || !cache->ubasis_k || !cache->ubasis_v)
+      return fail(KVS_ERR_ARG, "null factorized cache buffer");
+    if (!aligned16(q) || !aligned16(out) || !aligned4(seq_len) || !aligned16(cache->ck_pool) ||
+        !aligned16(cache->cv_pool) || !aligned16(cache->dk_pool) || !aligned16(cache->dv_pool) ||
+        !aligned16(cache->basis_k) || !aligned16(cache->basis_v) || !aligned16(cache->ubasis_k) ||
+        !aligned16(cache->ubasis_v) || !aligned16(cache->sk_pool) || !aligned16(cache->sv_pool) ||
+        !aligned16(cache->rank_pool) || !aligned4(cache->page_table))
+      return fail(KVS_ERR_ALIGN, "q, out and the factorized buffers must be 16-byte aligned");
+    FactPrefillLaunch f;
+    f.ck_pool = cache->ck_pool;
+    f.cv_pool = cache->cv_pool;
+    f.dk_pool = cache->dk_pool;
+    f.dv_pool = cache->dv_pool;
+    f.sk_pool = cache->sk_pool;
+    f.sv_pool = cache->sv_pool;
+    f.rank_pool = cache->rank_pool;
+    f.basis_k = cache->basis_k;
+    f.basis_v = cache->basis_v;
+    f.ubasis_k = cache->ubasis_k;
+    f.ubasis_v = cache->ubasis_v;
+    f.page_table = cache->page_table;
+    f.pages_per_seq = p.pages_per_seq;
+    f.n_phys_pages = p.n_phys_pages;
+    f.n_kv_heads = p.cfg.n_kv_heads;
+    f.n_q_heads = p.cfg.n_q_heads;
+    f.head_dim = p.cfg.head_dim;
+    f.coef_slot = li.src_slot[0];
+    f.layer = layer;
+    f.q = q;
+    f.n = n;
+    f.seq_len = seq_len;
+    f.max_ctx = p.cfg.max_ctx;
+    f.key_excl = li.masks_current;
+    f.batch = batch;
+    f.causal = causal != 0;
+    f.scale_log2 = scale_log2(p.cfg.head_dim);
+    f.out = out;
+    f.out_dtype = out_dtype;
+    return hip_status(launch_fact_prefill(f, stream), "factorized prefill launch");
+  }
+  if (p.cfg.dtype != KVS_BF16)
+    return fail(KVS_ERR_UNSUPPORTED, "prefill runs on bf16 caches (bf16 MFMA)");
   if (!prefill_shape_supported(p.cfg.head_dim, group))
     return fail(KVS_ERR_UNSUPPORTED, "no prefill kernel for this head_dim/group size");
   if (!cache->k_pool || !cache->v_pool || !cache->page_table) return fail(KVS_ERR_ARG, "null cache pool");
   if (!aligned16(q) || !aligned16(out) || !aligned16(cache->k_pool) || !aligned16(cache->v_pool) ||
       !aligned4(seq_len) || !aligned4(cache->page_table))
     return fail(KVS_ERR_ALIGN, "q, out and the pools must be 16-byte aligned");
-  const kvs_layer_info& li = p.layers[layer];
   PrefillLaunch a;
   a.k_pool = cache->k_pool;
   a.v_pool = cache->v_pool;

@@ -180,6 +180,36 @@ int launch_fact_decode(const FactDecodeLaunch& a, void* stream);
 bool fact_shape_supported(int32_t head_dim, int32_t group, int32_t basis_rank,
                           int32_t resid_rank_max);
 
+struct FactPrefillLaunch {
+  const void* ck_pool; const void* cv_pool;
+  const void* dk_pool; const void* dv_pool;
+  const void* sk_pool; const void* sv_pool;
+  const void* rank_pool;
+  const void* basis_k; const void* basis_v;
+  const void* ubasis_k; const void* ubasis_v;
+  const int32_t* page_table;
+  int32_t pages_per_seq;
+  int32_t n_phys_pages;
+  int32_t n_kv_heads;
+  int32_t n_q_heads;
+  int32_t head_dim;
+  int32_t coef_slot;
+  int32_t layer;
+  const void* q;
+  int32_t n;
+  const int32_t* seq_len;
+  int32_t max_ctx;
+  int32_t key_excl;            // 1: the current position is masked (source above the layer)
+  int32_t batch;
+  int32_t causal;
+  float scale_log2;
+  void* out;
+  int32_t out_dtype;
+};
+int launch_fact_prefill(const FactPrefillLaunch& a, void* stream);
+bool fact_prefill_shape_supported(int32_t head_dim, int32_t group, int32_t basis_rank,
+                                  int32_t resid_rank_max);
+
 const char* hip_error_name(int err);
 
 }  // namespace kvs

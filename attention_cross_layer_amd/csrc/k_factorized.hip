@@ -162,20 +162,10 @@ __device__ __forceinline__ float quad_row_sum(float x) {
   return x;
 }
 
-constexpr uint32_t kOOB = 0x80000000u;   // offset past every resource's end
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  typedef __attribute__((ext_vector_type(4))) uint32_t u4_t;
-  const u4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
-  return make_uint2(v.x, v.y);
-}
+using dev::kOOB;
+using dev::ld16;
+using dev::ld8;
+using dev::rsrc;
 
 // One page as loaded: cK, codes and meta with lane = token; cV with lane =
 // (quad, coefficient); the scales with lane = quad.

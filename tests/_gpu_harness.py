@@ -180,3 +180,14 @@ class Factorized:
         k, v = self.kv(layer)
         return A.attend_decode(q, k, v, self.lens.tolist(),
                                exclude_current=P.excludes_current(self.src.tolist(), self.w.tolist(), layer))
+
+    def prefill(self, layer, q, causal=True, out_dtype=torch.float32):
+        got = K.kvs_attn_prefill_chunk(self.plan, self.cache, layer, q.cuda(), self.seq_len,
+                                       causal=causal, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        return got
+
+    def oracle_prefill(self, layer, q, causal=True):
+        k, v = self.kv(layer)
+        return A.attend_prefill(q, k, v, self.lens.tolist(), causal=causal,
+                                exclude_current=P.excludes_current(self.src.tolist(), self.w.tolist(), layer))
