@@ -146,11 +146,13 @@ def cpu_baseline(wl, src, w, host_seq, budget_s=12.0):
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PREFILL_WORKLOAD = "depthgraft_prefill_chunk"
+FACT_PREFILL_WORKLOAD = "factorized_prefill_chunk"
+PREFILL_WORKLOADS = (PREFILL_WORKLOAD, FACT_PREFILL_WORKLOAD)
 CALIB_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"decode_kernel": "k_decode.hip", "decode_mfma_kernel": "k_decode.hip",
                   "fact_decode_kernel": "k_factorized.hip",
-                  "prefill_kernel": "k_prefill.hip"}
+                  "prefill_kernel": "k_prefill.hip", "fact_prefill_kernel": "k_fact_prefill.hip"}
 
 
 def source_digest(kernel):
@@ -223,6 +225,14 @@ def algorithmic_bytes(wl, kernel):
         sum_r = B * (16 * n_hi + 8 * ((T - n_hi) // 2))   # exact per-rank token counts
         tokens = B * T
         return wl.n_kv_heads * (tokens * (2 * wl.basis_rank * 2 + 4) + 2 * sum_r) + tokens
+    if kernel.startswith("fact_prefill_kernel"):
+        # queries in, outputs out (bf16), every coefficient row, code, scale
+        # and meta entry of the sequence once
+        n, T = wl.prefill_n, wl.ctx
+        n_hi = int(round(wl.rank16_frac * T))
+        sum_r = 16 * n_hi + 8 * ((T - n_hi) // 2)
+        return (n * wl.n_q_heads * wl.head_dim * 2 * 2
+                + wl.n_kv_heads * (T * (2 * wl.basis_rank * 2 + 4) + 2 * sum_r) + 2 * T)
     if kernel.startswith("prefill_kernel"):
         # queries in, outputs out (bf16), every K/V tile of the sequence once
         n, T = wl.prefill_n, wl.ctx
@@ -240,15 +250,15 @@ def record_profile(prof_dir, kernel, workload, s):
     import csv
     import glob
 
-    prefill = workload == PREFILL_WORKLOAD
-    wl = datagen.WORKLOADS["depthgraft"].with_(batch=1) if prefill else datagen.WORKLOADS[workload]
+    prefill = workload in PREFILL_WORKLOADS
+    wl = prefill_wl(workload) if prefill else datagen.WORKLOADS[workload]
     base = kernel.split("<")[0]
     f = glob.glob(os.path.join(prof_dir, "kt", "*kernel_stats.csv"))
     allk = sorted(csv.DictReader(open(f[0])), key=lambda r: -float(r["TotalDurationNs"]))
     top = [r for r in allk if "kvs::" in r["Name"]] + [r for r in allk if "kvs::" not in r["Name"]][:4]
     alg = algorithmic_bytes(wl, kernel)
     fetch, write = s["FETCH_SIZE"]["bytes_per_dispatch"], s["WRITE_SIZE"]["bytes_per_dispatch"]
-    cmd = ("python3 bench.py --prefill --steps 2 --warmup 1" if prefill
+    cmd = (f"python3 bench.py --workload {workload} --steps 2 --warmup 1" if prefill
            else f"python3 bench.py --workload {workload} --roofline-only")
     lines = [
         f"# `{kernel}` on `{workload}`", "",
@@ -265,12 +275,14 @@ def record_profile(prof_dir, kernel, workload, s):
         f"- FETCH_SIZE: {s['FETCH_SIZE']['kib_per_dispatch']:.1f} KiB/dispatch x "
         f"{s['FETCH_SIZE']['scale']:.4f} (copy calibration: 256 MiB read counted as "
         f"{s['FETCH_SIZE']['copy_kib']:.1f} KiB) = {fetch:,.0f} B "
-        f"({fetch / alg:.3f} x algorithmic)",
+        f"({fetch / alg:.3f} x the algorithmic bytes"
+        + (", which count reads and writes)" if prefill else ")"),
         f"- WRITE_SIZE: {s['WRITE_SIZE']['kib_per_dispatch']:.1f} KiB/dispatch x "
-        f"{s['WRITE_SIZE']['scale']:.4f} = {write:,.0f} B",
-        (f"- MFMA rate at the traced average: "
-         f"{prefill_flops(wl.prefill_n, wl.ctx, wl.n_q_heads, wl.head_dim) / (s['avg_us'] * 1e-6) / 1e12:,.0f}"
-         f" TFLOP/s ({prefill_flops(wl.prefill_n, wl.ctx, wl.n_q_heads, wl.head_dim) / (s['avg_us'] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS:.1%}"
+        f"{s['WRITE_SIZE']['scale']:.4f} = {write:,.0f} B"
+        + (f"; read + written = {(fetch + write) / alg:.3f} x algorithmic" if prefill else ""),
+        (f"- algorithmic MFMA rate at the traced average: "
+         f"{prefill_kernel_flops(wl, kernel) / (s['avg_us'] * 1e-6) / 1e12:,.0f}"
+         f" TFLOP/s ({prefill_kernel_flops(wl, kernel) / (s['avg_us'] * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS:.1%}"
          f" of 2.5 PFLOP/s bf16; the profiler slows this launch)" if prefill else
          f"- algorithmic rate at the traced average: {alg / (s['avg_us'] * 1e-6) / 1e9:,.0f} GB/s "
          f"({alg / (s['avg_us'] * 1e-6) / 1e9 / HBM_PEAK_GBS:.1%} of 8 TB/s)"), "",
@@ -322,33 +334,94 @@ def prefill_flops(n, T, n_q_heads, hd):
     return pairs * 4 * hd * n_q_heads
 
 
-def prefill_main(args):
-    """DepthGraft prefill: the second 4096-token chunk of an 8192-token prompt
-    (queries at 4096..8191, causal), batch 1, over the 16 owner layers (the
-    deeper layers own no cache entries, so prompt tokens need not run them).
-    A step appends the chunk's K/V to each owner layer and runs its
-    prefill-chunk attention."""
+def fact_prefill_flops(n, T, n_q_heads, hd, width=48):
+    """Algorithmic FLOPs of a causal chunk over the factorized cache in the
+    coefficient space: per unmasked (query, key) pair 2*width for the score
+    and 2*width for the value accumulation (width = basis rank + residual
+    rank bound); per query row 2*hd*width to project it onto the bases and
+    2*hd*width to map its accumulators back."""
+    pairs = n * (T - n) + n * (n + 1) // 2
+    return n_q_heads * (pairs * 4 * width + n * 4 * hd * width)
+
+
+def prefill_wl(workload):
+    """Workload of a prefill benchmark: the DepthGraft chunk (4096 queries at
+    offset 4096 of an 8192-token prompt, batch 1) or the same chunk on the
+    64K factorized model's shape."""
+    if workload == FACT_PREFILL_WORKLOAD:
+        return datagen.WORKLOADS["factorized_64k"].with_(batch=1, ctx=8192, prefill_n=4096,
+                                                         prefill_batch=1)
+    return datagen.WORKLOADS["depthgraft"].with_(batch=1)
+
+
+def prefill_kernel_flops(wl, kernel):
+    if kernel.startswith("fact_prefill_kernel"):
+        return fact_prefill_flops(wl.prefill_n, wl.ctx, wl.n_q_heads, wl.head_dim,
+                                  wl.basis_rank + wl.resid_rank_max)
+    return prefill_flops(wl.prefill_n, wl.ctx, wl.n_q_heads, wl.head_dim)
+
+
+def prefill_main(args, workload):
+    """Prefill-chunk attention over one chunk per layer that needs it.
+
+    depthgraft_prefill_chunk: the second 4096-token chunk of an 8192-token
+    prompt (queries at 4096..8191, causal), batch 1, over the 16 owner layers
+    of the DepthGraft map (the deeper layers own no cache entries, so prompt
+    tokens need not run them); a step appends the chunk's K/V to each owner
+    layer and runs its prefill-chunk attention.
+    factorized_prefill_chunk: the same chunk on the 64K factorized model's
+    shape (32 layers in 16 pairs, 32 q / 8 KV heads, hd 128, basis rank 32,
+    residual ranks 0/8/16); a step appends the chunk's factorized entries
+    (pair coefficients from the owner layer, each layer's codes and scales)
+    and runs every layer's prefill-chunk attention."""
     if args.gpus != 1:
         print("bench.py runs on one GPU only", file=sys.stderr)
         sys.exit(2)
-    wl = datagen.WORKLOADS["depthgraft"].with_(batch=1)
+    fact = workload == FACT_PREFILL_WORKLOAD
+    wl = prefill_wl(workload)
     n, T = wl.prefill_n, wl.ctx
     torch.cuda.set_device(0)
-    log(f"[bench] setting up {wl.name} prefill chunk n={n} at offset {T - n}")
-    src, w, plan, cache, owners = setup(wl)
-    qs = {l: datagen.prefill_q(wl, l, n, device="cuda") for l in owners}
-    chunk = {l: datagen.owner_kv(wl, l, device="cuda") for l in owners}
-    chunk = {l: (kv[0][:, T - n:].contiguous(), kv[1][:, T - n:].contiguous()) for l, kv in chunk.items()}
+    log(f"[bench] setting up {workload}: {wl.name} prefill chunk n={n} at offset {T - n}")
     start = torch.full((1,), T - n, dtype=torch.int32, device="cuda")
     seq_len = torch.full((1,), T, dtype=torch.int32, device="cuda")
-    outs = {l: torch.empty((1, n, wl.n_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
-            for l in owners}
     stream = torch.cuda.current_stream()
-    ev = {l: [] for l in owners}
+    if fact:
+        src, w, plan, cache, owners, rank = setup_factorized(wl)
+        layers = list(range(wl.n_layers))
+        r_chunk = rank[:, T - n:].contiguous()
+        chunk = {}
+        for l in layers:
+            cc = (tuple(x[:, T - n:].contiguous() for x in datagen.pair_coeffs(wl, l // 2, device="cuda"))
+                  if l in owners else (None, None))
+            res = tuple(x[:, T - n:].contiguous()
+                        for x in datagen.layer_residual(wl, l, rank, device="cuda"))
+            chunk[l] = cc + res
+
+        def append(l):
+            ck, cv, dk, dv, sk, sv = chunk[l]
+            K.kvs_append_factorized(plan, cache, l, ck, cv, dk, dv, sk, sv, r_chunk, start,
+                                    stream=stream)
+        flops = fact_prefill_flops(n, T, wl.n_q_heads, wl.head_dim, wl.basis_rank + wl.resid_rank_max)
+        kernel = "fact_prefill_kernel (bf16 MFMA in the coefficient space, causal)"
+    else:
+        src, w, plan, cache, owners = setup(wl)
+        layers = owners
+        chunk = {l: datagen.owner_kv(wl, l, device="cuda") for l in owners}
+        chunk = {l: (kv[0][:, T - n:].contiguous(), kv[1][:, T - n:].contiguous())
+                 for l, kv in chunk.items()}
+
+        def append(l):
+            K.kvs_append(plan, cache, l, chunk[l][0], chunk[l][1], start, stream=stream)
+        flops = prefill_flops(n, T, wl.n_q_heads, wl.head_dim)
+        kernel = "prefill_kernel (bf16 MFMA, causal)"
+    qs = {l: datagen.prefill_q(wl, l, n, device="cuda") for l in layers}
+    outs = {l: torch.empty((1, n, wl.n_q_heads, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+            for l in layers}
+    ev = {l: [] for l in layers}
 
     def step(record=False):
-        for l in owners:
-            K.kvs_append(plan, cache, l, chunk[l][0], chunk[l][1], start, stream=stream)
+        for l in layers:
+            append(l)
             if record:
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
@@ -368,24 +441,29 @@ def prefill_main(args):
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
-    us = sum(e0.elapsed_time(e1) for l in owners for (e0, e1) in ev[l]) * 1e3 / (
-        args.steps * len(owners))
-    flops = prefill_flops(n, T, wl.n_q_heads, wl.head_dim)
+    us = sum(e0.elapsed_time(e1) for l in layers for (e0, e1) in ev[l]) * 1e3 / (
+        args.steps * len(layers))
     achieved = flops / (us * 1e-6) / 1e12
     res = {"metric": "shared-KV prefill chunk attn: prefill tokens/s and MFMA utilisation",
            "value": n * 1000.0 / ms, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-           "config": {"workload": PREFILL_WORKLOAD, "owner_layers": len(owners),
+           "config": {"workload": workload, "layers": len(layers),
                       "batch": 1, "chunk": n, "ctx": T, "causal": True,
                       "q_heads": wl.n_q_heads, "kv_heads": wl.n_kv_heads,
                       "head_dim": wl.head_dim},
            "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                        "traffic": None, "kernel": "prefill_kernel (bf16 MFMA, causal)",
+                        "traffic": None, "kernel": kernel,
                         "flops_per_launch": flops, "avg_launch_us": us}}
+    if fact:
+        res["config"] |= {"basis_rank": wl.basis_rank, "resid_rank_max": wl.resid_rank_max,
+                          "rank16_frac": wl.rank16_frac}
+        # the rate of an attention over rebuilt hd-wide rows doing the same job
+        dense = prefill_flops(n, T, wl.n_q_heads, wl.head_dim)
+        res["roofline"]["dense_equivalent_tflops"] = dense / (us * 1e-6) / 1e12
     calibration_copy()
-    traffic = recorded_traffic(PREFILL_WORKLOAD)
+    traffic = recorded_traffic(workload)
     if traffic is not None:
         res["roofline"]["traffic"] = traffic["bytes_per_launch"]
         res["roofline"]["traffic_source"] = traffic["source"]
@@ -399,7 +477,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tinyllama_cla2",
                     choices=["tiny_cla2", "tinyllama_cla2", "depthgraft", "cla2_64k",
-                             "factorized_64k", "tinyllama_cla2_top", PREFILL_WORKLOAD])
+                             "factorized_64k", "tinyllama_cla2_top", *PREFILL_WORKLOADS])
     ap.add_argument("--roofline-passes", type=int, default=3)
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the cache-flushed per-launch timing loop (for profiling)")
@@ -422,8 +500,10 @@ def main():
         if args.record:
             print(record_profile(args.summarize, args.kernel, args.workload, s))
         return
-    if args.prefill or args.workload == PREFILL_WORKLOAD:
-        return prefill_main(args)
+    if args.workload in PREFILL_WORKLOADS:
+        return prefill_main(args, args.workload)
+    if args.prefill:
+        return prefill_main(args, PREFILL_WORKLOAD)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path is a "
               "single-GPU kernel library; sharding across GPUs is described, not built.",
