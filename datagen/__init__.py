@@ -47,6 +47,7 @@ PAGE = 64  # tokens per cache page / key block
 TAG_K, TAG_V, TAG_Q, TAG_QP, TAG_PEAK, TAG_MIX = 1, 2, 3, 4, 5, 6
 TAG_CK, TAG_CV, TAG_BK, TAG_BV, TAG_DK, TAG_DV = 11, 12, 13, 14, 15, 16
 TAG_SK, TAG_SV, TAG_UK, TAG_UV, TAG_RANK = 17, 18, 19, 20, 21
+TAG_PAIR_DIR, TAG_PAIR_LATENT, TAG_LAYER_DIR, TAG_LAYER_LATENT, TAG_NOISE = 22, 23, 24, 25, 26
 
 
 @dataclasses.dataclass(frozen=True)
@@ -289,6 +290,57 @@ def layer_residual(wl: Workload, layer: int, rank: torch.Tensor, device="cpu",
     sk = ((sk + 0.5) * (0.5 / 127.0)).to(torch.float16)
     sv = ((sv + 0.5) * (0.5 / 127.0)).to(torch.float16)
     return dk.to(torch.int8), dv.to(torch.int8), sk, sv
+
+
+def _orthonormal_rows(k: int, hd: int, g: torch.Generator, device) -> torch.Tensor:
+    """k random orthonormal rows [k, hd] (QR of a Gaussian matrix)."""
+    m = torch.randn((hd, k), generator=g, device=device, dtype=torch.float32)
+    q, r = torch.linalg.qr(m.cpu().double())
+    q = q * torch.sign(torch.diagonal(r))[None, :]
+    return q.T.to(torch.float32).to(device)
+
+
+def correlated_pair_rows(wl: Workload, pair: int, which: str, device="cpu",
+                         batch: Optional[int] = None, ctx: Optional[int] = None):
+    """Full K (which="k") or V ("v") rows of the two layers of a pair whose
+    states are strongly correlated, the situation the factorized cache
+    targets: [B, T, Hkv, hd] bf16 each, (rows of the lower layer, rows of the
+    upper layer).
+
+    Per KV head: a shared latent z_t in R^R with per-direction scales drawn
+    from U(1, 2) on R random orthonormal directions; the upper layer's latent
+    is z_t + 0.1 * N(0, 1) (per direction, scaled alike); each layer adds
+    Rmax layer-specific random directions with N(0, 1) * U(0.3, 0.45)
+    weights, and i.i.d. N(0, 0.02^2) noise on every channel.  With the
+    workload's R = 32, Rmax = 16 and hd = 128 this leaves a clear gap after
+    the R-th principal direction of the stacked rows and after the Rmax-th
+    of each layer's residual.
+    """
+    B = wl.batch if batch is None else batch
+    T = wl.ctx if ctx is None else ctx
+    Hkv, hd, R, Rm = wl.n_kv_heads, wl.head_dim, wl.basis_rank, wl.resid_rank_max
+    tw = 0 if which == "k" else 1
+    idx = 2 * pair + tw
+    gd = _gen(wl, TAG_PAIR_DIR, idx, "cpu")
+    shared = torch.stack([_orthonormal_rows(R, hd, gd, "cpu") for _ in range(Hkv)]).to(device)
+    sig = (1.0 + torch.rand((Hkv, R), generator=gd)).to(device)
+    z = torch.randn((B, T, Hkv, R), generator=_gen(wl, TAG_PAIR_LATENT, idx, device),
+                    device=device) * sig
+    out = []
+    for j in range(2):
+        lj = 4 * pair + 2 * j + tw
+        gl = _gen(wl, TAG_LAYER_DIR, lj, "cpu")
+        own = torch.stack([_orthonormal_rows(Rm, hd, gl, "cpu") for _ in range(Hkv)]).to(device)
+        tau = (0.3 + 0.15 * torch.rand((Hkv, Rm), generator=gl)).to(device)
+        gz = _gen(wl, TAG_LAYER_LATENT, lj, device)
+        zj = z if j == 0 else z + 0.1 * torch.randn(z.shape, generator=gz, device=device) * sig
+        w = torch.randn((B, T, Hkv, Rm), generator=gz, device=device) * tau
+        noise = 0.02 * torch.randn((B, T, Hkv, hd), generator=_gen(wl, TAG_NOISE, lj, device),
+                                   device=device)
+        x = (torch.einsum("btgi,gid->btgd", zj, shared) + torch.einsum("btgj,gjd->btgd", w, own)
+             + noise)
+        out.append(x.to(torch.bfloat16))
+    return out[0], out[1]
 
 
 def seq_lens(batch: int, ctx: int, ragged: bool = False, seed: int = 0, min_len: int = 1):

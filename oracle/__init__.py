@@ -14,9 +14,13 @@ The oracle computes the plain definitions, in float64, from logical
                     int8 residual) key/value reconstruction.
 * ``plan``       -- which layers own cached K/V, the owner-slot numbering and
                     the validity rules of a sharing map.
+* ``factorize``  -- the factorized cache's write side: a layer pair's basis,
+                    a layer's residual directions (leading singular vectors)
+                    and the encoder (pair coefficients, int8 residual codes,
+                    fp16 scale per token).
 
 Every function is pinned by the CPU tests to something other than itself
 (closed forms, a library routine, invariants, brute force); none is marked
 "parity unpinned".
 """
-from . import attention, plan  # noqa: F401
+from . import attention, factorize, plan  # noqa: F401
