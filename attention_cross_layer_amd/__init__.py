@@ -32,8 +32,9 @@ PAGE = 64
 # Every symbol include/kvshare.h declares.
 EXPORTS = ("kvs_share_plan", "kvs_plan_free", "kvs_plan_layer", "kvs_plan_summary",
            "kvs_cache_layout", "kvs_decode_splits", "kvs_decode_workspace_size", "kvs_append",
-           "kvs_append_factorized", "kvs_attn_decode", "kvs_attn_prefill_chunk",
-           "kvs_last_error")
+           "kvs_append_factorized", "kvs_encode_workspace_size", "kvs_encode_factorized",
+           "kvs_basis_workspace_size", "kvs_pair_basis", "kvs_residual_basis",
+           "kvs_attn_decode", "kvs_attn_prefill_chunk", "kvs_last_error")
 
 
 class KvsError(RuntimeError):
@@ -116,6 +117,13 @@ def lib():
                                   vp]),
         "kvs_attn_prefill_chunk": (i32, [vp, P(kvs_cache), i32, vp, i32, vp, i32, i32, vp, i32,
                                          vp]),
+        "kvs_encode_workspace_size": (i32, [vp, i32, i32, P(sz)]),
+        "kvs_encode_factorized": (i32, [vp, P(kvs_cache), i32, vp, vp, vp, vp, vp, i32, vp, i32,
+                                        vp, sz, vp]),
+        "kvs_basis_workspace_size": (i32, [vp, i32, i32, P(sz)]),
+        "kvs_pair_basis": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]),
+        "kvs_residual_basis": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, sz,
+                                     vp]),
         "kvs_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -132,7 +140,11 @@ def _check(status: int):
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the library must be contiguous (dense row-major)")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream):
@@ -283,6 +295,62 @@ def kvs_append_factorized(plan: Plan, cache: Cache, layer: int, ck, cv, dk, dv, 
     _check(lib().kvs_append_factorized(plan.handle, ctypes.byref(cache.struct), layer, _ptr(ck),
                                        _ptr(cv), _ptr(dk), _ptr(dv), _ptr(sk), _ptr(sv),
                                        _ptr(rank), n, _ptr(start_pos), B, _stream(stream)))
+
+
+def kvs_encode_workspace_size(plan: Plan, batch: int, n: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().kvs_encode_workspace_size(plan.handle, batch, n, ctypes.byref(out)))
+    return out.value
+
+
+def kvs_encode_factorized(plan: Plan, cache: Cache, layer: int, k: torch.Tensor, v: torch.Tensor,
+                          rank: torch.Tensor, start_pos: torch.Tensor, k_owner=None, v_owner=None,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """Encode k, v [B, n, Hkv, hd] (bf16) of ``layer`` into the factorized
+    cache at start_pos; k_owner / v_owner: rows of the pair's coefficient-
+    writing layer (None when ``layer`` is that layer)."""
+    B, n = k.shape[0], k.shape[1]
+    if workspace is None:
+        workspace = torch.empty(kvs_encode_workspace_size(plan, B, n), dtype=torch.uint8,
+                                device=k.device)
+    _check(lib().kvs_encode_factorized(plan.handle, ctypes.byref(cache.struct), layer, _ptr(k),
+                                       _ptr(v), _ptr(k_owner), _ptr(v_owner), _ptr(rank), n,
+                                       _ptr(start_pos), B, _ptr(workspace), workspace.numel(),
+                                       _stream(stream)))
+
+
+def kvs_basis_workspace_size(plan: Plan, batch: int, n: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().kvs_basis_workspace_size(plan.handle, batch, n, ctypes.byref(out)))
+    return out.value
+
+
+def kvs_pair_basis(plan: Plan, k_a, v_a, k_b, v_b, n_tokens: torch.Tensor, basis_k: torch.Tensor,
+                   basis_v: torch.Tensor, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Pair basis [Hkv, R, hd] (bf16, written into basis_k / basis_v) from the
+    rows [B, n, Hkv, hd] of the pair's two layers (k_b, v_b may be None)."""
+    B, n = k_a.shape[0], k_a.shape[1]
+    if workspace is None:
+        workspace = torch.empty(kvs_basis_workspace_size(plan, B, n), dtype=torch.uint8,
+                                device=k_a.device)
+    _check(lib().kvs_pair_basis(plan.handle, _ptr(k_a), _ptr(v_a), _ptr(k_b), _ptr(v_b),
+                                _ptr(n_tokens), n, B, _ptr(basis_k), _ptr(basis_v),
+                                _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def kvs_residual_basis(plan: Plan, k, v, basis_k, basis_v, n_tokens: torch.Tensor,
+                       ubasis_k: torch.Tensor, ubasis_v: torch.Tensor, k_owner=None,
+                       v_owner=None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Residual directions [Hkv, Rmax, hd] (bf16, written into ubasis_k /
+    ubasis_v) of a layer from its rows, the owner's rows and the pair basis."""
+    B, n = k.shape[0], k.shape[1]
+    if workspace is None:
+        workspace = torch.empty(kvs_basis_workspace_size(plan, B, n), dtype=torch.uint8,
+                                device=k.device)
+    _check(lib().kvs_residual_basis(plan.handle, _ptr(k), _ptr(v), _ptr(k_owner), _ptr(v_owner),
+                                    _ptr(basis_k), _ptr(basis_v), _ptr(n_tokens), n, B,
+                                    _ptr(ubasis_k), _ptr(ubasis_v), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
 
 
 def kvs_attn_decode(plan: Plan, cache: Cache, layer: int, q: torch.Tensor,

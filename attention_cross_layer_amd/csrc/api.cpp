@@ -323,3 +323,241 @@ extern "C" kvs_status kvs_append_factorized(const kvs_plan* plan, const kvs_cach
   a.max_ctx = p.cfg.max_ctx;
   return hip_status(launch_fact_append(a, stream), "factorized append launch");
 }
+
+// ------------------------------------------------------------- write side
+
+namespace {
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Encoder workspace: per side (K, V) the coefficients [B][n][Hkv][R] bf16,
+// codes [B][n][Hkv][Rmax] int8 and scales [B][n][Hkv] fp16.
+struct EncodeWs {
+  size_t c, d, s, total;
+};
+EncodeWs encode_ws(const Plan& p, int32_t batch, int32_t n) {
+  const size_t rows = (size_t)batch * n * p.cfg.n_kv_heads;
+  EncodeWs w;
+  w.c = round256(rows * p.cfg.basis_rank * 2);
+  w.d = round256(rows * p.cfg.resid_rank_max);
+  w.s = round256(rows * 2);
+  w.total = 2 * (w.c + w.d + w.s);
+  return w;
+}
+
+// Basis workspace: Gram matrices [2][Hkv][hd][hd] and eigenvalues [2][Hkv][hd]
+// (fp32), then, for residual directions, the residual rows [2][B][n][Hkv][hd].
+struct BasisWs {
+  size_t gram, evals, rows, total;
+};
+BasisWs basis_ws(const Plan& p, int32_t batch, int32_t n) {
+  const size_t hd = p.cfg.head_dim, H = p.cfg.n_kv_heads;
+  BasisWs w;
+  w.gram = round256(2 * H * hd * hd * 4);
+  w.evals = round256(2 * H * hd * 4);
+  w.rows = round256((size_t)batch * n * H * hd * 4);
+  w.total = w.gram + w.evals + 2 * w.rows;
+  return w;
+}
+
+kvs_status check_write_side(const kvs_plan* plan, int32_t batch, int32_t n) {
+  if (!plan) return fail(KVS_ERR_ARG, "null plan");
+  const Plan& p = plan->p;
+  if (p.cfg.kind != KVS_FACTORIZED) return fail(KVS_ERR_ARG, "needs a factorized plan");
+  if (!encode_shape_supported(p.cfg.head_dim, p.cfg.basis_rank, p.cfg.resid_rank_max))
+    return fail(KVS_ERR_UNSUPPORTED, "no write-side kernels for this head_dim / rank");
+  kvs_status st = check_batch(plan, batch);
+  if (st != KVS_OK) return st;
+  if (n < 1 || n > p.cfg.max_ctx) return fail(KVS_ERR_RANGE, "n out of range");
+  return KVS_OK;
+}
+
+}  // namespace
+
+extern "C" kvs_status kvs_encode_workspace_size(const kvs_plan* plan, int32_t batch, int32_t n,
+                                                size_t* bytes) {
+  clear_error();
+  kvs_status st = check_write_side(plan, batch, n);
+  if (st != KVS_OK) return st;
+  if (!bytes) return fail(KVS_ERR_ARG, "null argument");
+  *bytes = encode_ws(plan->p, batch, n).total;
+  return KVS_OK;
+}
+
+extern "C" kvs_status kvs_encode_factorized(const kvs_plan* plan, const kvs_cache* cache,
+                                            int32_t layer, const void* k, const void* v,
+                                            const void* k_owner, const void* v_owner,
+                                            const uint8_t* rank, int32_t n,
+                                            const int32_t* start_pos, int32_t batch,
+                                            void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  kvs_status st = check_layer(plan, layer);
+  if (st != KVS_OK) return st;
+  if ((st = check_write_side(plan, batch, n)) != KVS_OK) return st;
+  const Plan& p = plan->p;
+  const kvs_layer_info& li = p.layers[layer];
+  if (!cache || !k || !v || !rank || !start_pos || !workspace) return fail(KVS_ERR_ARG, "null argument");
+  if ((k_owner == nullptr) != (v_owner == nullptr)) return fail(KVS_ERR_ARG, "give both k_owner and v_owner, or neither");
+  if (!li.owns_kv && !k_owner)
+    return fail(KVS_ERR_ARG, "layer " + std::to_string(layer) +
+                                 " does not write its pair's coefficients: pass the writing layer's rows");
+  if (!cache->basis_k || !cache->basis_v || !cache->ubasis_k || !cache->ubasis_v || !cache->ck_pool ||
+      !cache->cv_pool || !cache->dk_pool || !cache->dv_pool || !cache->sk_pool || !cache->sv_pool ||
+      !cache->rank_pool || !cache->page_table)
+    return fail(KVS_ERR_ARG, "null factorized cache buffer");
+  if (!aligned16(k) || !aligned16(v) || (k_owner && (!aligned16(k_owner) || !aligned16(v_owner))) ||
+      !aligned16(workspace) || !aligned16(cache->basis_k) || !aligned16(cache->basis_v) ||
+      !aligned16(cache->ubasis_k) || !aligned16(cache->ubasis_v) || !aligned16(cache->ck_pool) ||
+      !aligned16(cache->cv_pool) || !aligned16(cache->dk_pool) || !aligned16(cache->dv_pool) ||
+      !aligned4(start_pos) || !aligned4(cache->page_table) || ((uintptr_t)cache->sk_pool & 1) ||
+      ((uintptr_t)cache->sv_pool & 1) || ((uintptr_t)cache->rank_pool & 1))
+    return fail(KVS_ERR_ALIGN, "rows, workspace, bases and pools must be 16-byte aligned");
+  const EncodeWs w = encode_ws(p, batch, n);
+  if (ws_bytes < w.total) return fail(KVS_ERR_RANGE, "workspace too small: need " + std::to_string(w.total));
+  const size_t hd = p.cfg.head_dim, H = p.cfg.n_kv_heads;
+  const int32_t slot = li.src_slot[0];
+  char* ws = static_cast<char*>(workspace);
+  EncodeLaunch e;
+  const void* x[2] = {k, v};
+  const void* xo[2] = {k_owner ? k_owner : k, v_owner ? v_owner : v};
+  const void* bases[2] = {cache->basis_k, cache->basis_v};
+  const void* ubases[2] = {cache->ubasis_k, cache->ubasis_v};
+  for (int side = 0; side < 2; ++side) {
+    char* base = ws + side * (w.c + w.d + w.s);
+    e.x[side] = x[side];
+    e.xo[side] = xo[side];
+    e.basis[side] = static_cast<const uint16_t*>(bases[side]) + (size_t)slot * H * p.cfg.basis_rank * hd;
+    e.ubasis[side] = static_cast<const uint16_t*>(ubases[side]) + (size_t)layer * H * p.cfg.resid_rank_max * hd;
+    e.c_out[side] = li.owns_kv ? base : nullptr;
+    e.d_out[side] = base + w.c;
+    e.s_out[side] = base + w.c + w.d;
+    e.e_out[side] = nullptr;
+  }
+  e.rank = rank;
+  e.n_tokens = nullptr;
+  e.n = n;
+  e.batch = batch;
+  e.n_kv_heads = p.cfg.n_kv_heads;
+  e.head_dim = p.cfg.head_dim;
+  e.residual_mode = 0;
+  if ((st = hip_status(launch_encode(e, stream), "encode launch")) != KVS_OK) return st;
+  return kvs_append_factorized(plan, cache, layer, e.c_out[0], e.c_out[1],
+                               static_cast<const int8_t*>(e.d_out[0]),
+                               static_cast<const int8_t*>(e.d_out[1]), e.s_out[0], e.s_out[1], rank,
+                               n, start_pos, batch, stream);
+}
+
+extern "C" kvs_status kvs_basis_workspace_size(const kvs_plan* plan, int32_t batch, int32_t n,
+                                               size_t* bytes) {
+  clear_error();
+  kvs_status st = check_write_side(plan, batch, n);
+  if (st != KVS_OK) return st;
+  if (!bytes) return fail(KVS_ERR_ARG, "null argument");
+  *bytes = basis_ws(plan->p, batch, n).total;
+  return KVS_OK;
+}
+
+namespace {
+
+kvs_status check_basis_common(const kvs_plan* plan, const int32_t* n_tokens, int32_t n, int32_t batch,
+                              void* out_k, void* out_v, void* workspace, size_t ws_bytes) {
+  kvs_status st = check_write_side(plan, batch, n);
+  if (st != KVS_OK) return st;
+  if (!n_tokens || !out_k || !out_v || !workspace) return fail(KVS_ERR_ARG, "null argument");
+  if (!aligned4(n_tokens) || !aligned16(out_k) || !aligned16(out_v) || !aligned16(workspace))
+    return fail(KVS_ERR_ALIGN, "outputs and workspace must be 16-byte aligned");
+  const BasisWs w = basis_ws(plan->p, batch, n);
+  if (ws_bytes < w.total) return fail(KVS_ERR_RANGE, "workspace too small: need " + std::to_string(w.total));
+  return KVS_OK;
+}
+
+BasisLaunch basis_launch(const Plan& p, const int32_t* n_tokens, int32_t n, int32_t batch, int32_t k_out,
+                         void* out_k, void* out_v, void* workspace) {
+  const BasisWs w = basis_ws(p, batch, n);
+  char* ws = static_cast<char*>(workspace);
+  BasisLaunch b;
+  b.n_tokens = n_tokens;
+  b.n = n;
+  b.batch = batch;
+  b.n_kv_heads = p.cfg.n_kv_heads;
+  b.head_dim = p.cfg.head_dim;
+  b.k_out = k_out;
+  b.gram = reinterpret_cast<float*>(ws);
+  b.evals = reinterpret_cast<float*>(ws + w.gram);
+  b.out[0] = out_k;
+  b.out[1] = out_v;
+  return b;
+}
+
+}  // namespace
+
+extern "C" kvs_status kvs_pair_basis(const kvs_plan* plan, const void* k_a, const void* v_a,
+                                     const void* k_b, const void* v_b, const int32_t* n_tokens,
+                                     int32_t n, int32_t batch, void* basis_k, void* basis_v,
+                                     void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  kvs_status st = check_basis_common(plan, n_tokens, n, batch, basis_k, basis_v, workspace, ws_bytes);
+  if (st != KVS_OK) return st;
+  if (!k_a || !v_a) return fail(KVS_ERR_ARG, "null argument");
+  if ((k_b == nullptr) != (v_b == nullptr)) return fail(KVS_ERR_ARG, "give both k_b and v_b, or neither");
+  if (!aligned16(k_a) || !aligned16(v_a) || (k_b && (!aligned16(k_b) || !aligned16(v_b))))
+    return fail(KVS_ERR_ALIGN, "rows must be 16-byte aligned");
+  BasisLaunch b = basis_launch(plan->p, n_tokens, n, batch, plan->p.cfg.basis_rank, basis_k, basis_v,
+                               workspace);
+  b.x[0][0] = k_a;
+  b.x[0][1] = k_b;
+  b.x[1][0] = v_a;
+  b.x[1][1] = v_b;
+  b.rows_f32 = 0;
+  return hip_status(launch_basis(b, stream), "pair basis launch");
+}
+
+extern "C" kvs_status kvs_residual_basis(const kvs_plan* plan, const void* k, const void* v,
+                                         const void* k_owner, const void* v_owner,
+                                         const void* basis_k, const void* basis_v,
+                                         const int32_t* n_tokens, int32_t n, int32_t batch,
+                                         void* ubasis_k, void* ubasis_v, void* workspace,
+                                         size_t ws_bytes, void* stream) {
+  clear_error();
+  kvs_status st = check_basis_common(plan, n_tokens, n, batch, ubasis_k, ubasis_v, workspace, ws_bytes);
+  if (st != KVS_OK) return st;
+  if (!k || !v || !basis_k || !basis_v) return fail(KVS_ERR_ARG, "null argument");
+  if ((k_owner == nullptr) != (v_owner == nullptr)) return fail(KVS_ERR_ARG, "give both k_owner and v_owner, or neither");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(basis_k) || !aligned16(basis_v) ||
+      (k_owner && (!aligned16(k_owner) || !aligned16(v_owner))))
+    return fail(KVS_ERR_ALIGN, "rows and bases must be 16-byte aligned");
+  const Plan& p = plan->p;
+  const BasisWs w = basis_ws(p, batch, n);
+  char* ws = static_cast<char*>(workspace);
+  float* rows[2] = {reinterpret_cast<float*>(ws + w.gram + w.evals),
+                    reinterpret_cast<float*>(ws + w.gram + w.evals + w.rows)};
+  EncodeLaunch e;
+  const void* x[2] = {k, v};
+  const void* xo[2] = {k_owner ? k_owner : k, v_owner ? v_owner : v};
+  const void* bases[2] = {basis_k, basis_v};
+  for (int side = 0; side < 2; ++side) {
+    e.x[side] = x[side];
+    e.xo[side] = xo[side];
+    e.basis[side] = bases[side];
+    e.ubasis[side] = nullptr;
+    e.c_out[side] = nullptr;
+    e.d_out[side] = nullptr;
+    e.s_out[side] = nullptr;
+    e.e_out[side] = rows[side];
+  }
+  e.rank = nullptr;
+  e.n_tokens = n_tokens;
+  e.n = n;
+  e.batch = batch;
+  e.n_kv_heads = p.cfg.n_kv_heads;
+  e.head_dim = p.cfg.head_dim;
+  e.residual_mode = 1;
+  if ((st = hip_status(launch_encode(e, stream), "residual rows launch")) != KVS_OK) return st;
+  BasisLaunch b = basis_launch(p, n_tokens, n, batch, p.cfg.resid_rank_max, ubasis_k, ubasis_v, workspace);
+  b.x[0][0] = rows[0];
+  b.x[0][1] = nullptr;
+  b.x[1][0] = rows[1];
+  b.x[1][1] = nullptr;
+  b.rows_f32 = 1;
+  return hip_status(launch_basis(b, stream), "residual basis launch");
+}

@@ -210,6 +210,43 @@ int launch_fact_prefill(const FactPrefillLaunch& a, void* stream);
 bool fact_prefill_shape_supported(int32_t head_dim, int32_t group, int32_t basis_rank,
                                   int32_t resid_rank_max);
 
+// Encoder: side 0 = K, side 1 = V.
+struct EncodeLaunch {
+  const void* x[2];            // [B][n][Hkv][hd] bf16 rows of the layer
+  const void* xo[2];           // rows of the pair's coefficient-writing layer
+  const void* basis[2];        // [Hkv][R][hd] bf16
+  const void* ubasis[2];       // [Hkv][Rmax][hd] bf16 (codes mode)
+  void* c_out[2];              // [B][n][Hkv][R] bf16 or null
+  void* d_out[2];              // [B][n][Hkv][Rmax] int8
+  void* s_out[2];              // [B][n][Hkv] fp16
+  float* e_out[2];             // residual mode: [B][n][Hkv][hd] fp32
+  const uint8_t* rank;         // [B][n]
+  const int32_t* n_tokens;     // residual mode: [B]
+  int32_t n;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t residual_mode;
+};
+int launch_encode(const EncodeLaunch& a, void* stream);
+bool encode_shape_supported(int32_t head_dim, int32_t basis_rank, int32_t resid_rank_max);
+
+// Basis builder: Gram matrices of the rows, then leading eigenvectors.
+struct BasisLaunch {
+  const void* x[2][2];         // [side][source] rows, [B][n][Hkv][hd]; source 1 may be null
+  int32_t rows_f32;            // rows are fp32 (residual rows) instead of bf16
+  const int32_t* n_tokens;     // [B]
+  int32_t n;
+  int32_t batch;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t k_out;
+  float* gram;                 // workspace [2][Hkv][hd][hd]
+  float* evals;                // workspace [2][Hkv][hd]
+  void* out[2];                // [Hkv][k_out][hd] bf16
+};
+int launch_basis(const BasisLaunch& a, void* stream);
+
 const char* hip_error_name(int err);
 
 }  // namespace kvs

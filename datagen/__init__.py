@@ -339,7 +339,7 @@ def correlated_pair_rows(wl: Workload, pair: int, which: str, device="cpu",
                                    device=device)
         x = (torch.einsum("btgi,gid->btgd", zj, shared) + torch.einsum("btgj,gjd->btgd", w, own)
              + noise)
-        out.append(x.to(torch.bfloat16))
+        out.append(x.to(torch.bfloat16).contiguous())
     return out[0], out[1]
 
 

@@ -61,8 +61,8 @@ typedef enum {
                                layer that owns no cache entries                 */
   KVS_ERR_RANGE = 4,        /* count beyond cache capacity or workspace size    */
   KVS_ERR_UNSUPPORTED = 5,  /* valid request this build does not implement
-                               (a source above its reader, an unsupported
-                               head_dim / group size / dtype combination)       */
+                               (an unsupported head_dim / group size / dtype /
+                               rank combination)                                */
   KVS_ERR_ALIGN = 6,        /* a device pointer is not 16-byte aligned          */
   KVS_ERR_HIP = 7           /* a HIP launch failed                              */
 } kvs_status;
@@ -129,7 +129,8 @@ typedef struct {
  *     rank (the meta pool) [n_phys_pages][64] uint16 = r_t | o_t << 8 (shared
  *          by all layers and heads)
  *     BK / BV  [n_slots][Hkv][R][hd] bf16;  UK / UV  [n_layers][Hkv][Rmax][hd]
- *          bf16 (written by the caller)                                    */
+ *          bf16 (written by the caller, e.g. with kvs_pair_basis and
+ *          kvs_residual_basis)                                             */
 typedef struct {
   int32_t page_tokens;         /* 64                                           */
   int32_t pages_per_seq;       /* ceil(max_ctx / 64)                           */
@@ -238,6 +239,77 @@ KVS_API kvs_status kvs_append_factorized(const kvs_plan* plan, const kvs_cache* 
                                          const int32_t* start_pos, int32_t batch,
                                          void* stream);
 
+/* --------------------------------------------- factorized write side (encoder)
+ * The factorized cache of "DepthWeave-KV: Smarter KV Cache Compression by
+ * Sharing Across Layers and Adapting Per Token" (Core Mechanism): a channel
+ * basis computed from a pair of neighbouring layers' own K/V, without
+ * training, and a small low-rank quantized residual per layer.  The page
+ * gives no numerical recipe; these calls implement the readings
+ *   c_t = bf16(B x^o_t), x^o the rows of the layer that writes the pair's
+ *         coefficients (the slot owner);
+ *   y_t = U_l (x_t - c_t B);  s_t = fp16(max_{j<r_t} |y_tj| / 127);
+ *   d_tj = clamp(round_half_even(y_tj / s_t), -127, 127) for j < r_t, else 0
+ *         (s_t = 0 and no codes when r_t = 0 or the maximum is 0);
+ *   B = the R leading right singular vectors of the pair's token rows
+ *       stacked (uncentred), U_l = the Rmax leading right singular vectors of
+ *       layer l's residual rows x_t - c_t B, per KV head, largest first, each
+ *       row's largest-magnitude entry positive, rounded to bf16.
+ * Products in the encoder run in fp32 (bf16 MFMA with the residual split into
+ * a bf16 high part and remainder); the basis builder accumulates fp32 Gram
+ * matrices and diagonalizes them with fp32 Jacobi rotations.                */
+
+/* Workspace bytes kvs_encode_factorized needs for (batch, n). */
+KVS_API kvs_status kvs_encode_workspace_size(const kvs_plan* plan, int32_t batch, int32_t n,
+                                             size_t* bytes);
+
+/* Encode n new tokens of `layer` from its K/V rows and append them
+ * (coefficients when the layer owns its pair's slot, codes, scales, rank).
+ *   k, v             device bf16 [batch][n][Hkv][hd]: the layer's rows
+ *   k_owner, v_owner rows of the layer owning the pair's slot for the same
+ *                    tokens (NULL when `layer` is that layer); the
+ *                    coefficients are recomputed from them exactly as the
+ *                    owner's call stored them
+ *   rank             device uint8 [batch][n], as kvs_append_factorized
+ *   start_pos        as kvs_append
+ *   workspace        device, >= kvs_encode_workspace_size(batch, n) bytes
+ * The bases are read from the cache (BK/BV of the pair's slot, UK/UV of the
+ * layer).  Errors: non-factorized plan, or a non-owner layer without owner
+ * rows -> KVS_ERR_ARG; head_dim not 64/128 or ranks not 32/16 ->
+ * KVS_ERR_UNSUPPORTED; otherwise as kvs_append_factorized. */
+KVS_API kvs_status kvs_encode_factorized(const kvs_plan* plan, const kvs_cache* cache,
+                                         int32_t layer, const void* k, const void* v,
+                                         const void* k_owner, const void* v_owner,
+                                         const uint8_t* rank, int32_t n,
+                                         const int32_t* start_pos, int32_t batch,
+                                         void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes kvs_pair_basis / kvs_residual_basis need for (batch, n). */
+KVS_API kvs_status kvs_basis_workspace_size(const kvs_plan* plan, int32_t batch, int32_t n,
+                                            size_t* bytes);
+
+/* Pair basis (K and V) from the rows of the pair's two layers.
+ *   k_a, v_a, k_b, v_b  device bf16 [batch][n][Hkv][hd]; k_b / v_b NULL for
+ *                       a single layer
+ *   n_tokens            device int32 [batch]: rows t < n_tokens[b] count
+ *   basis_k, basis_v    device bf16 [Hkv][R][hd] out (e.g. the slot's BK/BV)
+ * Fewer counted rows than R leave the trailing rows an arbitrary orthonormal
+ * completion. */
+KVS_API kvs_status kvs_pair_basis(const kvs_plan* plan, const void* k_a, const void* v_a,
+                                  const void* k_b, const void* v_b, const int32_t* n_tokens,
+                                  int32_t n, int32_t batch, void* basis_k, void* basis_v,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
+/* Residual directions (UK and UV) of a layer from its rows, the slot owner's
+ * rows (NULL when the layer is the owner) and the pair basis (bf16
+ * [Hkv][R][hd], as stored).  ubasis_k / ubasis_v: device bf16
+ * [Hkv][Rmax][hd] out. */
+KVS_API kvs_status kvs_residual_basis(const kvs_plan* plan, const void* k, const void* v,
+                                      const void* k_owner, const void* v_owner,
+                                      const void* basis_k, const void* basis_v,
+                                      const int32_t* n_tokens, int32_t n, int32_t batch,
+                                      void* ubasis_k, void* ubasis_v, void* workspace,
+                                      size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- attention */
 
 /* One decode query per (sequence, q head) of `layer` over keys
@@ -266,7 +338,12 @@ KVS_API kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cache,
  *   q        device bf16 [batch][n][Hq][hd]
  *   seq_len  device int32 [batch], each >= n
  *   out      device [batch][n][Hq][hd] of out_dtype
- * Dense bf16 plans only (KVS_ERR_UNSUPPORTED otherwise). */
+ * Dense bf16 plans, and factorized plans (head_dim 64/128, ranks 32/16),
+ * which attend in the coefficient space: q~ = B^K q and u~ = U^K q once per
+ * query, scores c_t . q~ + s_t (d_t . u~), value accumulators in the 48
+ * coefficients mapped back through B^V and U^V once per query row; q~, u~ and
+ * the scaled codes s_t d_t enter the MFMA as bf16.  Other plans ->
+ * KVS_ERR_UNSUPPORTED. */
 KVS_API kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cache* cache,
                                           int32_t layer, const void* q, int32_t n,
                                           const int32_t* seq_len, int32_t batch,

@@ -191,3 +191,44 @@ class Factorized:
         k, v = self.kv(layer)
         return A.attend_prefill(q, k, v, self.lens.tolist(), causal=causal,
                                 exclude_current=P.excludes_current(self.src.tolist(), self.w.tolist(), layer))
+
+
+def unpack_factorized(cache, layer, slot, B, n, Hkv, start=0):
+    """Read back the factorized entries of positions start..start+n-1 of every
+    sequence (page table of ``cache``) into dense host arrays, following the
+    documented pool layout: coefficients of ``slot`` (cK, cV: [B,n,Hkv,32]
+    bf16 as float64), codes of ``layer`` (dK, dV: [B,n,Hkv,16] int), scales
+    (sK, sV: [B,n,Hkv] float64) and ranks [B,n]."""
+    sz = cache.sizes
+    P_ = sz.n_phys_pages
+    pt = cache.page_table.cpu()
+    ckp = cache.ck_pool.cpu().view(torch.bfloat16).view(-1, P_, Hkv, 64 * 32).double().numpy()
+    cvp = cache.cv_pool.cpu().view(torch.bfloat16).view(-1, P_, Hkv, 64 * 32).double().numpy()
+    dkp = cache.dk_pool.cpu().view(torch.int8).view(-1, P_, Hkv, 128 * 8).numpy().astype(np.int64)
+    dvp = cache.dv_pool.cpu().view(torch.int8).view(-1, P_, Hkv, 128 * 8).numpy().astype(np.int64)
+    skp = cache.sk_pool.cpu().view(torch.float16).view(-1, P_, Hkv, 64).double().numpy()
+    svp = cache.sv_pool.cpu().view(torch.float16).view(-1, P_, Hkv, 64).double().numpy()
+    meta = cache.rank_pool.cpu().view(torch.int16).view(P_, 64).numpy().astype(np.int64) & 0xffff
+    ck = np.zeros((B, n, Hkv, 32)); cv = np.zeros((B, n, Hkv, 32))
+    dk = np.zeros((B, n, Hkv, 16), dtype=np.int64); dv = np.zeros((B, n, Hkv, 16), dtype=np.int64)
+    sk = np.zeros((B, n, Hkv)); sv = np.zeros((B, n, Hkv))
+    rank = np.zeros((B, n), dtype=np.int64)
+    i_idx = np.arange(32)
+    m = i_idx // 4
+    for b in range(B):
+        for i in range(n):
+            pos = start + i
+            page, t = int(pt[b, pos // 64]), pos % 64
+            r, o = int(meta[page, t]) & 0xff, int(meta[page, t]) >> 8
+            rank[b, i] = r
+            cvo = ((m // 2) * 64 + 4 * (t // 4) + i_idx % 4) * 8 + (m % 2) * 4 + t % 4
+            cko = ((i_idx // 8) * 64 + t) * 8 + i_idx % 8
+            for h in range(Hkv):
+                ck[b, i, h] = ckp[slot, page, h, cko]
+                cv[b, i, h] = cvp[slot, page, h, cvo]
+                nb = 8 * ((r + 7) // 8)
+                dk[b, i, h, :nb] = dkp[layer, page, h, o * 8:o * 8 + nb]
+                dv[b, i, h, :nb] = dvp[layer, page, h, o * 8:o * 8 + nb]
+                sk[b, i, h] = skp[layer, page, h, t]
+                sv[b, i, h] = svp[layer, page, h, t]
+    return ck, cv, dk, dv, sk, sv, rank
