@@ -328,32 +328,51 @@ struct EigParams {
   int32_t max_sweeps;
 };
 
-// one workgroup of 1024 threads per matrix: blockIdx.x = side * Hkv + head
+// one workgroup of 1024 threads per matrix: blockIdx.x = side * Hkv + head.
+// Each round rotates 64 disjoint index pairs at once: every 2x2 block
+// A[{p_i,q_i}, {p_j,q_j}] becomes J_i^T A J_j (one read and one write of the
+// block), and V's columns p_i, q_i rotate.  A pair is rotated only while its
+// coupling is above 1e-6 sqrt(a_pp a_qq) and above 2e-7 of the matrix's
+// Frobenius norm (about the fp32 rounding level of the entries, so the
+// eigenvectors of well-separated leading eigenvalues come out to ~1e-5); the
+// sweeps stop after one without a rotation.
 template <int HD>
 __global__ __launch_bounds__(1024) void eig_kernel(EigParams a) {
   constexpr int NP = HD / 2;           // disjoint pairs per round
   constexpr int LD = HD + 1;
   __shared__ float A[HD * LD];
   __shared__ float V[HD * LD];
-  __shared__ float cs[NP], sn[NP];
-  __shared__ int pp[NP], qq[NP];
-  __shared__ float red[2][32];
+  __shared__ float2 rot[NP];           // (c, s) of each pair this round
+  __shared__ int2 pq[NP];              // (p, q)
+  __shared__ float red[16];
   __shared__ int order[HD];
   __shared__ float sgn[HD];
-  __shared__ int done;
+  __shared__ int rotated;
+  __shared__ float floor_abs;
 
   const int tid = threadIdx.x;
   const int side = blockIdx.x / a.n_kv_heads, h = blockIdx.x % a.n_kv_heads;
   const float* g = a.gram + (size_t)blockIdx.x * HD * HD;
+  float ss = 0.f;
   for (int idx = tid; idx < HD * HD; idx += 1024) {
     const int r = idx / HD, c = idx % HD;
-    A[r * LD + c] = g[idx];
+    const float v = g[idx];
+    A[r * LD + c] = v;
     V[r * LD + c] = r == c ? 1.f : 0.f;
+    ss += v * v;
   }
-  if (tid == 0) done = 0;
+  ss = dev::wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.f;
+    for (int w = 0; w < 16; ++w) t += red[w];
+    floor_abs = 2e-7f * sqrtf(t);
+  }
   __syncthreads();
 
   for (int sweep = 0; sweep < a.max_sweeps; ++sweep) {
+    if (tid == 0) rotated = 0;
     for (int round = 0; round < HD - 1; ++round) {
       // round-robin pairing: index HD-1 is fixed, the others rotate
       if (tid < NP) {
@@ -366,75 +385,56 @@ __global__ __launch_bounds__(1024) void eig_kernel(EigParams a) {
           q = (round - tid + (HD - 1)) % (HD - 1);
         }
         const float apq = A[p * LD + q];
+        const float app = A[p * LD + p], aqq = A[q * LD + q];
         float c = 1.f, s = 0.f;
-        if (apq != 0.f) {
-          const float app = A[p * LD + p], aqq = A[q * LD + q];
+        if (fabsf(apq) > fmaxf(1e-6f * sqrtf(fabsf(app * aqq)), floor_abs)) {
           const float tau = (aqq - app) / (2.f * apq);
           const float at = fabsf(tau);
           const float t = (at > 1e15f ? 0.5f / at : 1.f / (at + sqrtf(1.f + tau * tau))) *
                           (tau >= 0.f ? 1.f : -1.f);
           c = 1.f / sqrtf(1.f + t * t);
           s = t * c;
+          rotated = 1;
         }
-        cs[tid] = c;
-        sn[tid] = s;
-        pp[tid] = p;
-        qq[tid] = q;
+        rot[tid] = make_float2(c, s);
+        pq[tid] = make_int2(p, q);
       }
       __syncthreads();
-      // A <- A J and V <- V J: columns p, q of every row
-      {
-        const int k = tid % NP;
-        const float c = cs[k], s = sn[k];
-        const int p = pp[k], q = qq[k];
-        for (int r = tid / NP; r < HD; r += 1024 / NP) {
-          const float ap = A[r * LD + p], aq = A[r * LD + q];
-          A[r * LD + p] = c * ap - s * aq;
-          A[r * LD + q] = s * ap + c * aq;
-          const float vp = V[r * LD + p], vq = V[r * LD + q];
-          V[r * LD + p] = c * vp - s * vq;
-          V[r * LD + q] = s * vp + c * vq;
-        }
+      // A <- J^T A J, one 2x2 block per (i, j); this thread's j is fixed
+      // (1024 is a multiple of NP), a wave shares i
+      const int j = tid % NP;
+      const float2 rj = rot[j];
+      const int2 ij = pq[j];
+      const float cj = rj.x, sj = rj.y;
+      const int pj = ij.x, qj = ij.y;
+      for (int i = tid / NP; i < NP; i += 1024 / NP) {
+        const float2 ri = rot[i];
+        const int2 ii = pq[i];
+        const float ci = ri.x, si = ri.y;
+        const int pi = ii.x, qi = ii.y;
+        const float a00 = A[pi * LD + pj], a01 = A[pi * LD + qj];
+        const float a10 = A[qi * LD + pj], a11 = A[qi * LD + qj];
+        const float m00 = cj * a00 - sj * a01, m01 = sj * a00 + cj * a01;
+        const float m10 = cj * a10 - sj * a11, m11 = sj * a10 + cj * a11;
+        // the rotated pair's own coupling is zero by construction; storing
+        // the rounded remainder instead would keep a tiny eigenvalue paired
+        // with a large one above the relative threshold
+        const bool own = i == j && si != 0.f;
+        A[pi * LD + pj] = ci * m00 - si * m10;
+        A[pi * LD + qj] = own ? 0.f : ci * m01 - si * m11;
+        A[qi * LD + pj] = own ? 0.f : si * m00 + ci * m10;
+        A[qi * LD + qj] = si * m01 + ci * m11;
       }
-      __syncthreads();
-      // A <- J^T A: rows p, q of every column
-      {
-        const int cc = tid % HD;
-        for (int k = tid / HD; k < NP; k += 1024 / HD) {
-          const float c = cs[k], s = sn[k];
-          const int p = pp[k], q = qq[k];
-          const float ap = A[p * LD + cc], aq = A[q * LD + cc];
-          A[p * LD + cc] = c * ap - s * aq;
-          A[q * LD + cc] = s * ap + c * aq;
-        }
+      // V <- V J: columns p_j, q_j of every row
+      for (int r = tid / NP; r < HD; r += 1024 / NP) {
+        const float vp = V[r * LD + pj], vq = V[r * LD + qj];
+        V[r * LD + pj] = cj * vp - sj * vq;
+        V[r * LD + qj] = sj * vp + cj * vq;
       }
       __syncthreads();
     }
-    // converged when the off-diagonal mass is below 1e-12 of the total
-    float off = 0.f, tot = 0.f;
-    for (int idx = tid; idx < HD * HD; idx += 1024) {
-      const int r = idx / HD, c = idx % HD;
-      const float v = A[r * LD + c];
-      tot += v * v;
-      if (r != c) off += v * v;
-    }
-    off = dev::wave_sum(off);
-    tot = dev::wave_sum(tot);
-    if ((tid & 63) == 0) {
-      red[0][tid >> 6] = off;
-      red[1][tid >> 6] = tot;
-    }
+    if (!rotated) break;
     __syncthreads();
-    if (tid == 0) {
-      float o = 0.f, t = 0.f;
-      for (int w = 0; w < 16; ++w) {
-        o += red[0][w];
-        t += red[1][w];
-      }
-      done = o <= 1e-12f * t;
-    }
-    __syncthreads();
-    if (done) break;
   }
 
   // ---- order by eigenvalue, largest first (ties: lower index first)
@@ -538,7 +538,7 @@ int launch_basis(const BasisLaunch& a, void* stream) {
   e.out[0] = static_cast<uint16_t*>(a.out[0]);
   e.out[1] = static_cast<uint16_t*>(a.out[1]);
   e.evals = a.evals;
-  e.max_sweeps = 24;
+  e.max_sweeps = 20;
   int err;
   if (a.head_dim == 64) {
     if ((err = run_gram<64>(g, st)) != 0) return err;

@@ -148,11 +148,14 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 PREFILL_WORKLOAD = "depthgraft_prefill_chunk"
 FACT_PREFILL_WORKLOAD = "factorized_prefill_chunk"
 PREFILL_WORKLOADS = (PREFILL_WORKLOAD, FACT_PREFILL_WORKLOAD)
+ENCODE_WORKLOAD = "factorized_encode_chunk"
+N_BASIS_STREAMS = 4
 CALIB_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"decode_kernel": "k_decode.hip", "decode_mfma_kernel": "k_decode.hip",
                   "fact_decode_kernel": "k_factorized.hip",
-                  "prefill_kernel": "k_prefill.hip", "fact_prefill_kernel": "k_fact_prefill.hip"}
+                  "prefill_kernel": "k_prefill.hip", "fact_prefill_kernel": "k_fact_prefill.hip",
+                  "encode_kernel": "k_encode.hip"}
 
 
 def source_digest(kernel):
@@ -470,6 +473,148 @@ def prefill_main(args, workload):
     print(json.dumps(res), flush=True)
 
 
+def encode_call_bytes(wl, n, owner):
+    """Algorithmic HBM bytes of one kvs_encode_factorized call over n tokens
+    (batch 1): K and V rows of the layer in, and of the coefficient-writing
+    layer when it is another one; the cache entries out (coefficients when
+    the layer owns the pair's slot, ceil(r/8) code granules, a scale per
+    token and KV head, the meta entry)."""
+    H, hd = wl.n_kv_heads, wl.head_dim
+    n_hi = int(round(wl.rank16_frac * n))
+    granule_bytes = 8 * (2 * n_hi + (n - n_hi) // 2)          # ranks 16 / 8 / 0
+    rows = 2 * n * H * hd * 2 * (1 if owner else 2)
+    out = 2 * (H * (granule_bytes + 2 * n) + (n * H * wl.basis_rank * 2 if owner else 0)) + 2 * n
+    return rows + out
+
+
+def encode_main(args):
+    """Factorized write path over a 4096-token prompt chunk on the 64K
+    factorized model's shape (32 layers in 16 pairs, 32 q / 8 KV heads, hd
+    128, basis rank 32, residual ranks 0/8/16 by seeded rank): a step encodes
+    the chunk's K/V rows of every layer into the cache (kvs_encode_factorized;
+    the pair's lower layer writes the coefficients, the upper one passes the
+    lower layer's rows).  The bases of every pair and layer are built once
+    from the same rows (kvs_pair_basis, kvs_residual_basis) and timed
+    separately."""
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only", file=sys.stderr)
+        sys.exit(2)
+    n = 4096
+    wl = datagen.WORKLOADS["factorized_64k"].with_(batch=1, ctx=n)
+    torch.cuda.set_device(0)
+    log(f"[bench] setting up {ENCODE_WORKLOAD}: {n} tokens x {wl.n_layers} layers")
+    src, w = datagen.share_map(wl)
+    cfg = K.make_config(wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, "bf16", 1, n,
+                        kind=K.KVS_FACTORIZED, basis_rank=wl.basis_rank,
+                        resid_rank_max=wl.resid_rank_max)
+    plan = K.kvs_share_plan(cfg, src, w)
+    cache = K.Cache(plan, "cuda")
+    owners = datagen.owner_layers(src)
+    rows = {}
+    for pair in range(wl.n_layers // 2):
+        ka, kb = datagen.correlated_pair_rows(wl, pair, "k", device="cuda")
+        va, vb = datagen.correlated_pair_rows(wl, pair, "v", device="cuda")
+        rows[2 * pair], rows[2 * pair + 1] = (ka, va), (kb, vb)
+    rank = datagen.token_ranks(wl, device="cuda")
+    start = torch.zeros(1, dtype=torch.int32, device="cuda")
+    n_tok = torch.full((1,), n, dtype=torch.int32, device="cuda")
+    Hkv, R, Rm, hd = wl.n_kv_heads, wl.basis_rank, wl.resid_rank_max, wl.head_dim
+    bk = cache.basis_k.view(torch.bfloat16).view(len(owners), Hkv, R, hd)
+    bv = cache.basis_v.view(torch.bfloat16).view(len(owners), Hkv, R, hd)
+    uk = cache.ubasis_k.view(torch.bfloat16).view(wl.n_layers, Hkv, Rm, hd)
+    uv = cache.ubasis_v.view(torch.bfloat16).view(wl.n_layers, Hkv, Rm, hd)
+    ews = torch.empty(K.kvs_encode_workspace_size(plan, 1, n), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    # the pairs are independent: their bases are built on N_BASIS_STREAMS
+    # streams (default priority), each with its own workspace
+    side = [torch.cuda.Stream() for _ in range(N_BASIS_STREAMS)]
+    bws = [torch.empty(K.kvs_basis_workspace_size(plan, 1, n), dtype=torch.uint8, device="cuda")
+           for _ in side]
+
+    def owner_of(l):
+        return int(src[l, 0])
+
+    def build_bases():
+        start_ev = torch.cuda.Event()
+        start_ev.record(stream)
+        for st in side:
+            st.wait_event(start_ev)
+        for idx, o in enumerate(owners):
+            st, ws = side[idx % len(side)], bws[idx % len(side)]
+            (ka, va), (kb, vb) = rows[o], rows[o + 1]
+            slot = owners.index(o)
+            K.kvs_pair_basis(plan, ka, va, kb, vb, n_tok, bk[slot], bv[slot], workspace=ws,
+                             stream=st)
+            for l in (o, o + 1):
+                k, v = rows[l]
+                K.kvs_residual_basis(plan, k, v, bk[slot], bv[slot], n_tok, uk[l], uv[l],
+                                     k_owner=None if l == o else ka,
+                                     v_owner=None if l == o else va, workspace=ws, stream=st)
+        for st in side:
+            done_ev = torch.cuda.Event()
+            done_ev.record(st)
+            stream.wait_event(done_ev)
+
+    build_bases()
+    torch.cuda.synchronize()
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    build_bases()
+    b1.record(stream)
+    torch.cuda.synchronize()
+    basis_ms = b0.elapsed_time(b1)
+
+    ev = {l: [] for l in range(wl.n_layers)}
+
+    def step(record=False):
+        for l in range(wl.n_layers):
+            k, v = rows[l]
+            o = owner_of(l)
+            ko, vo = (None, None) if o == l else rows[o]
+            if record:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            K.kvs_encode_factorized(plan, cache, l, k, v, rank, start, k_owner=ko, v_owner=vo,
+                                    workspace=ews, stream=stream)
+            if record:
+                e1.record(stream)
+                ev[l].append((e0, e1))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step(record=True)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    per = {l: sum(e0.elapsed_time(e1) for e0, e1 in ev[l]) * 1e3 / args.steps for l in ev}
+    upper = [l for l in range(wl.n_layers) if owner_of(l) != l]
+    us = sum(per[l] for l in upper) / len(upper)
+    nbytes = encode_call_bytes(wl, n, owner=False)
+    achieved = nbytes / (us * 1e-6) / 1e9
+    res = {"metric": "factorized cache write path: encoded tokens/s (all layers) and HBM GB/s",
+           "value": n * 1000.0 / ms, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": ENCODE_WORKLOAD, "layers": wl.n_layers, "batch": 1, "chunk": n,
+                      "kv_heads": Hkv, "head_dim": hd, "basis_rank": R, "resid_rank_max": Rm,
+                      "rank16_frac": wl.rank16_frac},
+           "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                        "kernel": "kvs_encode_factorized call of an upper pair layer "
+                                  "(encode_kernel + fact_append_kernel)",
+                        "bytes_per_launch": nbytes, "avg_launch_us": us,
+                        "owner_layer_avg_us": sum(per[l] for l in owners) / len(owners)},
+           "basis_build_ms": basis_ms,
+           "basis_build": f"{len(owners)} pair bases + {wl.n_layers} residual bases "
+                          f"(K and V) from {n} rows per layer, pairs spread over "
+                          f"{N_BASIS_STREAMS} streams"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -477,7 +622,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="tinyllama_cla2",
                     choices=["tiny_cla2", "tinyllama_cla2", "depthgraft", "cla2_64k",
-                             "factorized_64k", "tinyllama_cla2_top", *PREFILL_WORKLOADS])
+                             "factorized_64k", "tinyllama_cla2_top", *PREFILL_WORKLOADS,
+                             ENCODE_WORKLOAD])
     ap.add_argument("--roofline-passes", type=int, default=3)
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the cache-flushed per-launch timing loop (for profiling)")
@@ -500,6 +646,8 @@ def main():
         if args.record:
             print(record_profile(args.summarize, args.kernel, args.workload, s))
         return
+    if args.workload == ENCODE_WORKLOAD:
+        return encode_main(args)
     if args.workload in PREFILL_WORKLOADS:
         return prefill_main(args, args.workload)
     if args.prefill:
