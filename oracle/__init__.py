@@ -18,9 +18,11 @@ The oracle computes the plain definitions, in float64, from logical
                     a layer's residual directions (leading singular vectors)
                     and the encoder (pair coefficients, int8 residual codes,
                     fp16 scale per token).
+* ``router``     -- the token router's attention statistics (entropy, peak
+                    probability of each decode query) and its rank choice.
 
 Every function is pinned by the CPU tests to something other than itself
 (closed forms, a library routine, invariants, brute force); none is marked
 "parity unpinned".
 """
-from . import attention, factorize, plan  # noqa: F401
+from . import attention, factorize, plan, router  # noqa: F401
