@@ -34,7 +34,8 @@ EXPORTS = ("kvs_share_plan", "kvs_plan_free", "kvs_plan_layer", "kvs_plan_summar
            "kvs_cache_layout", "kvs_decode_splits", "kvs_decode_workspace_size", "kvs_append",
            "kvs_append_factorized", "kvs_encode_workspace_size", "kvs_encode_factorized",
            "kvs_basis_workspace_size", "kvs_pair_basis", "kvs_residual_basis",
-           "kvs_attn_decode", "kvs_attn_prefill_chunk", "kvs_last_error")
+           "kvs_attn_decode", "kvs_attn_decode_stats", "kvs_route_ranks",
+           "kvs_attn_prefill_chunk", "kvs_last_error")
 
 
 class KvsError(RuntimeError):
@@ -73,6 +74,12 @@ class kvs_cache(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "k_pool", "v_pool", "page_table", "ck_pool", "cv_pool", "dk_pool", "dv_pool", "sk_pool",
         "sv_pool", "rank_pool", "basis_k", "basis_v", "ubasis_k", "ubasis_v")]
+
+
+class kvs_router(ctypes.Structure):
+    _fields_ = [("entropy_focused", ctypes.c_float), ("entropy_diffuse", ctypes.c_float),
+                ("peak_focused", ctypes.c_float), ("rank_focused", ctypes.c_int32),
+                ("rank_mid", ctypes.c_int32), ("rank_diffuse", ctypes.c_int32)]
 
 
 _lib = None
@@ -124,6 +131,9 @@ def lib():
         "kvs_pair_basis": (i32, [vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]),
         "kvs_residual_basis": (i32, [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, sz,
                                      vp]),
+        "kvs_attn_decode_stats": (i32, [vp, P(kvs_cache), i32, vp, vp, i32, i32, i32, vp, i32, vp,
+                                        vp, sz, vp]),
+        "kvs_route_ranks": (i32, [vp, vp, i32, vp, i32, P(kvs_router), vp, vp]),
         "kvs_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -372,6 +382,44 @@ def kvs_attn_decode(plan: Plan, cache: Cache, layer: int, q: torch.Tensor,
                                  _dtype_code(out.dtype), _ptr(workspace), workspace.numel(),
                                  _stream(stream)))
     return out
+
+
+def kvs_attn_decode_stats(plan: Plan, cache: Cache, layer: int, q: torch.Tensor,
+                          seq_len: torch.Tensor, max_seq_len: int,
+                          out: Optional[torch.Tensor] = None, stats: Optional[torch.Tensor] = None,
+                          out_dtype=torch.float32, n_splits: int = 0,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """Factorized decode attention of ``layer`` plus per (sequence, query
+    head) attention statistics: returns (out [B, Hq, hd], stats [B, Hq, 2] =
+    entropy in nats, peak probability)."""
+    B, Hq = q.shape[0], q.shape[1]
+    if n_splits == 0:
+        n_splits = kvs_decode_splits(plan, B, max_seq_len)
+    if workspace is None:
+        workspace = torch.zeros(kvs_decode_workspace_size(plan, B, n_splits), dtype=torch.uint8,
+                                device=q.device)
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if stats is None:
+        stats = torch.empty((B, Hq, 2), dtype=torch.float32, device=q.device)
+    _check(lib().kvs_attn_decode_stats(plan.handle, ctypes.byref(cache.struct), layer, _ptr(q),
+                                       _ptr(seq_len), B, max_seq_len, n_splits, _ptr(out),
+                                       _dtype_code(out.dtype), _ptr(stats), _ptr(workspace),
+                                       workspace.numel(), _stream(stream)))
+    return out, stats
+
+
+def kvs_route_ranks(plan: Plan, stats: torch.Tensor, n_keys: torch.Tensor, router: kvs_router,
+                    rank_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Residual rank [B] (uint8) of each sequence's current token from
+    statistics [n_sets, B, Hq, 2] (or [B, Hq, 2]) and the keys each query saw."""
+    st = stats if stats.dim() == 4 else stats.unsqueeze(0)
+    n_sets, B = st.shape[0], st.shape[1]
+    if rank_out is None:
+        rank_out = torch.empty(B, dtype=torch.uint8, device=stats.device)
+    _check(lib().kvs_route_ranks(plan.handle, _ptr(st), n_sets, _ptr(n_keys), B,
+                                 ctypes.byref(router), _ptr(rank_out), _stream(stream)))
+    return rank_out
 
 
 def kvs_attn_prefill_chunk(plan: Plan, cache: Cache, layer: int, q: torch.Tensor,

@@ -1,6 +1,7 @@
 // C ABI glue: host-side argument validation (before any HIP call) and the
 // dispatch to the gfx950 launchers.  Pure C++; the launchers live in the .hip
 // files.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <string>
@@ -72,12 +73,12 @@ extern "C" kvs_status kvs_append(const kvs_plan* plan, const kvs_cache* cache, i
   return hip_status(launch_append(a, stream), "append launch");
 }
 
-extern "C" kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cache, int32_t layer,
-                                      const void* q, const int32_t* seq_len, int32_t batch,
-                                      int32_t max_seq_len, int32_t n_splits, void* out,
-                                      int32_t out_dtype, void* workspace, size_t ws_bytes,
-                                      void* stream) {
-  clear_error();
+namespace {
+
+kvs_status decode_impl(const kvs_plan* plan, const kvs_cache* cache, int32_t layer, const void* q,
+                       const int32_t* seq_len, int32_t batch, int32_t max_seq_len, int32_t n_splits,
+                       void* out, int32_t out_dtype, float* stats, void* workspace, size_t ws_bytes,
+                       void* stream) {
   kvs_status st = check_layer(plan, layer);
   if (st != KVS_OK) return st;
   const Plan& p = plan->p;
@@ -136,8 +137,10 @@ extern "C" kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cac
     f.ws = static_cast<float*>(workspace);
     f.out = out;
     f.out_dtype = out_dtype;
+    f.stats = stats;
     return hip_status(launch_fact_decode(f, stream), "factorized decode launch");
   }
+  if (stats) return fail(KVS_ERR_UNSUPPORTED, "router statistics are produced for factorized plans");
   if (!cache->k_pool || !cache->v_pool || !cache->page_table) return fail(KVS_ERR_ARG, "null cache pool");
   if (!aligned16(cache->k_pool) || !aligned16(cache->v_pool) || !aligned4(cache->page_table))
     return fail(KVS_ERR_ALIGN, "pools must be 16-byte aligned");
@@ -169,6 +172,61 @@ extern "C" kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cac
   a.out = out;
   a.out_dtype = out_dtype;
   return hip_status(launch_decode(a, stream), "decode launch");
+}
+
+}  // namespace
+
+extern "C" kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cache, int32_t layer,
+                                      const void* q, const int32_t* seq_len, int32_t batch,
+                                      int32_t max_seq_len, int32_t n_splits, void* out,
+                                      int32_t out_dtype, void* workspace, size_t ws_bytes,
+                                      void* stream) {
+  clear_error();
+  return decode_impl(plan, cache, layer, q, seq_len, batch, max_seq_len, n_splits, out, out_dtype,
+                     nullptr, workspace, ws_bytes, stream);
+}
+
+extern "C" kvs_status kvs_attn_decode_stats(const kvs_plan* plan, const kvs_cache* cache,
+                                            int32_t layer, const void* q, const int32_t* seq_len,
+                                            int32_t batch, int32_t max_seq_len, int32_t n_splits,
+                                            void* out, int32_t out_dtype, float* stats,
+                                            void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (!stats) return fail(KVS_ERR_ARG, "null stats");
+  if (!aligned4(stats)) return fail(KVS_ERR_ALIGN, "stats must be 4-byte aligned");
+  return decode_impl(plan, cache, layer, q, seq_len, batch, max_seq_len, n_splits, out, out_dtype,
+                     stats, workspace, ws_bytes, stream);
+}
+
+extern "C" kvs_status kvs_route_ranks(const kvs_plan* plan, const float* stats, int32_t n_sets,
+                                      const int32_t* n_keys, int32_t batch,
+                                      const kvs_router* router, uint8_t* rank_out, void* stream) {
+  clear_error();
+  if (!plan || !stats || !n_keys || !router || !rank_out) return fail(KVS_ERR_ARG, "null argument");
+  const Plan& p = plan->p;
+  if (p.cfg.kind != KVS_FACTORIZED) return fail(KVS_ERR_ARG, "ranks route a factorized plan");
+  kvs_status st = check_batch(plan, batch);
+  if (st != KVS_OK) return st;
+  if (n_sets < 1) return fail(KVS_ERR_RANGE, "n_sets must be >= 1");
+  if (!std::isfinite(router->entropy_focused) || !std::isfinite(router->entropy_diffuse) ||
+      std::isnan(router->peak_focused))
+    return fail(KVS_ERR_ARG, "router thresholds must be numbers");
+  if (!aligned4(stats) || !aligned4(n_keys)) return fail(KVS_ERR_ALIGN, "stats and n_keys must be 4-byte aligned");
+  RouteLaunch r;
+  r.stats = stats;
+  r.n_sets = n_sets;
+  r.n_keys = n_keys;
+  r.batch = batch;
+  r.n_q_heads = p.cfg.n_q_heads;
+  r.entropy_focused = router->entropy_focused;
+  r.entropy_diffuse = router->entropy_diffuse;
+  r.peak_focused = router->peak_focused;
+  const int32_t rmax = p.cfg.resid_rank_max;
+  r.rank_focused = std::min(std::max(router->rank_focused, 0), rmax);
+  r.rank_mid = std::min(std::max(router->rank_mid, 0), rmax);
+  r.rank_diffuse = std::min(std::max(router->rank_diffuse, 0), rmax);
+  r.rank_out = rank_out;
+  return hip_status(launch_route(r, stream), "route launch");
 }
 
 extern "C" kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cache* cache,

@@ -175,6 +175,7 @@ struct FactDecodeLaunch {
   float* ws;
   void* out;
   int32_t out_dtype;
+  float* stats;                // [B][Hq][2] entropy, peak probability; or null
 };
 int launch_fact_decode(const FactDecodeLaunch& a, void* stream);
 bool fact_shape_supported(int32_t head_dim, int32_t group, int32_t basis_rank,
@@ -246,6 +247,18 @@ struct BasisLaunch {
   void* out[2];                // [Hkv][k_out][hd] bf16
 };
 int launch_basis(const BasisLaunch& a, void* stream);
+
+struct RouteLaunch {
+  const float* stats;          // [n_sets][B][Hq][2]
+  int32_t n_sets;
+  const int32_t* n_keys;       // [B]
+  int32_t batch;
+  int32_t n_q_heads;
+  float entropy_focused, entropy_diffuse, peak_focused;
+  int32_t rank_focused, rank_mid, rank_diffuse;
+  uint8_t* rank_out;           // [B]
+};
+int launch_route(const RouteLaunch& a, void* stream);
 
 const char* hip_error_name(int err);
 

@@ -91,6 +91,8 @@ struct FactParams {
   float* ws_c;          // [B][Hq][S][48]
   float* ws_m;          // [B][Hq][S]
   float* ws_l;          // [B][Hq][S]
+  float* ws_a;          // [B][Hq][S]: sum_t p_t (z_t - m) (statistics only)
+  float* stats;         // [B][Hq][2]: entropy (nats), peak probability; or null
   void* out;
   int32_t out_bf16;
 };
@@ -201,15 +203,28 @@ __device__ void project_out(const FactParams& a, int b, int kvh, const float* co
 
 // grid (S, Hkv, B), 4 waves; wave w walks pages pb+w, pb+w+4, ... of its
 // partition, with the next page's loads in flight while it computes one.
-template <int HD, int G>
+// entropy ln l - ln2 A / l (nats) and peak probability 1 / l of one query row
+// from its softmax sum l and A = sum_t p_t (z_t - m); (0, 0) without keys
+__device__ __forceinline__ void write_stats(float* stats, size_t row, float l, float A) {
+  const bool any = l > 0.f;
+  stats[2 * row] = any ? logf(l) - 0.69314718055994531f * A / l : 0.f;
+  stats[2 * row + 1] = any ? 1.f / l : 0.f;
+}
+
+// STATS: also track A = sum_t p_t (z_t - m) beside the sum l = sum_t p_t
+// (z in log2 units), so that the attention's entropy is ln l - ln2 A / l and
+// its peak probability 1 / l (the largest p_t is 2^0 = 1).
+template <int HD, int G, bool STATS>
 __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
   constexpr int NB = (G + 3) / 4;              // blocks of 4 query heads
   __shared__ float qt[NB * 4][kW];             // (B^K q, U^K q) * log2(e)/sqrt(hd)
   __shared__ float part[4][4][NB * 4][kW];     // [wave][16-lane row][head][coefficient]
   __shared__ float part_l[4][4][NB * 4];
+  __shared__ float part_a[STATS ? 4 : 1][4][NB * 4];
   __shared__ float wave_m[4][NB * 4];
   __shared__ float fin_c[G * kW];
   __shared__ float fin_l[G];
+  __shared__ float fin_a[G];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -333,12 +348,13 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
   const uint32_t sel1 = (pos & 2) ? 0x03020706u : 0x05040100u;
   const uint32_t sel2 = (pos & 1) ? 0x03070105u : 0x06020400u;
 
-  float m_run[NB], l_run[NB];
+  float m_run[NB], l_run[NB], a_run[NB];
   f4_t acc[NB][12];
 #pragma unroll
   for (int hb = 0; hb < NB; ++hb) {
     m_run[hb] = -INFINITY;
     l_run[hb] = 0.f;
+    a_run[hb] = 0.f;
 #pragma unroll
     for (int m = 0; m < 12; ++m) acc[hb][m] = f4_t{0.f, 0.f, 0.f, 0.f};
   }
@@ -426,6 +442,7 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
       const float mu = mn == -INFINITY ? 0.f : mn;
       // 1 exactly while the max holds (also for heads past G, whose max stays -inf)
       const float alpha = m_run[hb] == mn ? 1.f : dev::fast_exp2(m_run[hb] - mu);
+      const float m_old = m_run[hb];
       m_run[hb] = mn;
       if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
         // accumulator entry e of every lane belongs to head e of the block:
@@ -442,6 +459,8 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
           acc[hb][m][2] *= a2;
           acc[hb][m][3] *= a3;
         }
+        // A refers to the new maximum: alpha (A + (m_old - m_new) l)
+        if (STATS) a_run[hb] = m_old == -INFINITY ? 0.f : alpha * fmaf(m_old - mu, l_run[hb], a_run[hb]);
         l_run[hb] *= alpha;
       }
       float p[4];
@@ -452,6 +471,13 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
       const float q0 = dev::bf16_lo(ap0), q1 = dev::bf16_hi(ap0);
       const float q2 = dev::bf16_lo(ap1), q3 = dev::bf16_hi(ap1);
       l_run[hb] += (q0 + q1) + (q2 + q3);
+      if (STATS) {
+        // masked tokens (z = -inf, p = 0) add nothing
+        float dz[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dz[e] = z[e] == -INFINITY ? 0.f : z[e] - mu;
+        a_run[hb] = fmaf(q0, dz[0], fmaf(q1, dz[1], fmaf(q2, dz[2], fmaf(q3, dz[3], a_run[hb]))));
+      }
       // p * s^V; masked tokens (p = 0) must not pick up a NaN scale
       const uint32_t as0 = pack_bf16(q0 * svf[0], q1 * svf[1]) & mk0;
       const uint32_t as1 = pack_bf16(q2 * svf[2], q3 * svf[3]) & mk1;
@@ -494,6 +520,10 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
         if (writer) part[wave][row][hb * 4 + e][4 * m + pos] = x;
       }
     if (writer) part_l[wave][row][hb * 4 + pos] = l;
+    if (STATS) {
+      const float aa = quad_row_sum(a_run[hb]);
+      if (writer) part_a[wave][row][hb * 4 + pos] = aa;
+    }
     if (lane < 4) wave_m[wave][hb * 4 + lane] = m_run[hb];
   }
   __syncthreads();
@@ -505,7 +535,7 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
     float M = wave_m[0][h];
 #pragma unroll
     for (int w = 1; w < 4; ++w) M = fmaxf(M, wave_m[w][h]);
-    float c = 0.f, l = 0.f;
+    float c = 0.f, l = 0.f, A = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -514,22 +544,31 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
         const float lw = (part_l[w][0][h] + part_l[w][1][h]) + (part_l[w][2][h] + part_l[w][3][h]);
         c = fmaf(f, cw, c);
         l = fmaf(f, lw, l);
+        if (STATS && i == 0 && wave_m[w][h] != -INFINITY) {
+          const float aw = (part_a[w][0][h] + part_a[w][1][h]) + (part_a[w][2][h] + part_a[w][3][h]);
+          A = fmaf(f, fmaf(wave_m[w][h] - M, lw, aw), A);
+        }
       }
     }
     if (S == 1) {
       fin_c[e] = c;
-      if (i == 0) fin_l[h] = l;
+      if (i == 0) {
+        fin_l[h] = l;
+        fin_a[h] = A;
+      }
     } else {
       const size_t rw = (hq0 + h) * S + split;
       a.ws_c[rw * kW + i] = c;
       if (i == 0) {
         a.ws_m[rw] = M;
         a.ws_l[rw] = l;
+        if (STATS) a.ws_a[rw] = A;
       }
     }
   }
   if (S != 1) return;
   __syncthreads();
+  if (STATS && tid < G) write_stats(a.stats, hq0 + tid, fin_l[tid], fin_a[tid]);
   project_out<HD, G>(a, b, kvh, fin_c, fin_l, tid, 256);
 }
 
@@ -539,10 +578,11 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
 // between them and folds each batch into a running (M, c, l); the basis
 // column each thread projects with (its d is fixed: 256 is a multiple of HD)
 // is loaded up front.  Partition order is fixed: deterministic.
-template <int HD, int G>
+template <int HD, int G, bool STATS>
 __global__ __launch_bounds__(256) void fact_merge_kernel(FactParams a) {
   static_assert(256 % HD == 0, "a thread keeps one output column");
   __shared__ float den[G];
+  __shared__ float num_a[G];
   __shared__ float coef[G * kW];
   const int tid = threadIdx.x;
   const int kvh = blockIdx.x, b = blockIdx.y;
@@ -563,7 +603,9 @@ __global__ __launch_bounds__(256) void fact_merge_kernel(FactParams a) {
     const float* mrow = a.ws_m + (hq0 + h) * S;
     const float* lrow = a.ws_l + (hq0 + h) * S;
     const float* crow = a.ws_c + (hq0 + h) * S * kW + i;
-    float M = -INFINITY, c = 0.f, l = 0.f;
+    const float* arow = a.ws_a + (hq0 + h) * S;
+    const bool with_a = STATS && i == 0;
+    float M = -INFINITY, c = 0.f, l = 0.f, A = 0.f;
     for (int s0 = 0; s0 < S; s0 += 16) {
       float mv[16], lv[16], cv[16];
 #pragma unroll
@@ -578,6 +620,7 @@ __global__ __launch_bounds__(256) void fact_merge_kernel(FactParams a) {
       for (int k = 0; k < 16; ++k) Mn = fmaxf(Mn, mv[k]);
       if (Mn != -INFINITY) {
         const float r = dev::fast_exp2(M - Mn);   // 0 while M is -inf
+        if (with_a) A = M == -INFINITY ? 0.f : r * fmaf(M - Mn, l, A);
         c *= r;
         l *= r;
 #pragma unroll
@@ -585,14 +628,17 @@ __global__ __launch_bounds__(256) void fact_merge_kernel(FactParams a) {
           const float f = dev::fast_exp2(mv[k] - Mn);   // 0 for empty or absent partitions
           c = fmaf(f, cv[k], c);
           l = fmaf(f, lv[k], l);
+          if (with_a && mv[k] != -INFINITY) A = fmaf(f, fmaf(mv[k] - Mn, lv[k], arow[s0 + k]), A);
         }
         M = Mn;
       }
     }
     coef[e] = c;
     if (i == 0) den[h] = l;
+    if (with_a) num_a[h] = A;
   }
   __syncthreads();
+  if (STATS && tid < G) write_stats(a.stats, hq0 + tid, den[tid], num_a[tid]);
   for (int h = tid / HD; h < G; h += 256 / HD) {
     float acc = 0.f;
 #pragma unroll
@@ -602,14 +648,19 @@ __global__ __launch_bounds__(256) void fact_merge_kernel(FactParams a) {
   }
 }
 
-template <int HD, int G>
-int run_fact(const FactParams& p, int B, hipStream_t st) {
-  hipLaunchKernelGGL((fact_decode_kernel<HD, G>), dim3(p.n_splits, p.n_kv_heads, B), dim3(256), 0,
-                     st, p);
+template <int HD, int G, bool STATS>
+int run_fact_t(const FactParams& p, int B, hipStream_t st) {
+  hipLaunchKernelGGL((fact_decode_kernel<HD, G, STATS>), dim3(p.n_splits, p.n_kv_heads, B), dim3(256),
+                     0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return (int)e;
-  hipLaunchKernelGGL((fact_merge_kernel<HD, G>), dim3(p.n_kv_heads, B), dim3(256), 0, st, p);
+  hipLaunchKernelGGL((fact_merge_kernel<HD, G, STATS>), dim3(p.n_kv_heads, B), dim3(256), 0, st, p);
   return (int)hipGetLastError();
+}
+
+template <int HD, int G>
+int run_fact(const FactParams& p, int B, hipStream_t st) {
+  return p.stats ? run_fact_t<HD, G, true>(p, B, st) : run_fact_t<HD, G, false>(p, B, st);
 }
 
 typedef int (*FactFn)(const FactParams&, int, hipStream_t);
@@ -748,6 +799,8 @@ int launch_fact_decode(const FactDecodeLaunch& a, void* stream) {
   p.ws_c = a.ws;
   p.ws_m = a.ws + rows * kW;
   p.ws_l = p.ws_m + rows;
+  p.ws_a = p.ws_l + rows;
+  p.stats = a.stats;
   p.out = a.out;
   p.out_bf16 = a.out_dtype == KVS_BF16;
   return fn(p, a.batch, static_cast<hipStream_t>(stream));

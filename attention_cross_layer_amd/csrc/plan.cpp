@@ -201,7 +201,10 @@ extern "C" kvs_status kvs_decode_workspace_size(const kvs_plan* plan, int32_t ba
   const kvs_config& c = plan->p.cfg;
   // a factorized plan's partial results live in the R + Rmax coefficient space
   const int32_t width = c.kind == KVS_DENSE ? c.head_dim : c.basis_rank + c.resid_rank_max;
-  *bytes = size_t(batch) * c.n_q_heads * n_splits * (width + 2) * sizeof(float);
+  // per partition row: the partial result, its maximum and sum, and for a
+  // factorized plan the entropy accumulator of the router statistics
+  const int32_t extra = c.kind == KVS_DENSE ? 2 : 3;
+  *bytes = size_t(batch) * c.n_q_heads * n_splits * (width + extra) * sizeof(float);
   return KVS_OK;
 }
 

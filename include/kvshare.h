@@ -350,6 +350,56 @@ KVS_API kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cache*
                                           int32_t causal, void* out, int32_t out_dtype,
                                           void* stream);
 
+/* --------------------------------------------------------- token router
+ * The token router of "DepthWeave-KV: Smarter KV Cache Compression by Sharing
+ * Across Layers and Adapting Per Token" (Core Mechanism, Key Concepts) reads
+ * attention statistics, entropy and peak scores, and gives focused tokens a
+ * higher residual rank, generic ones a lower one, online at every generation
+ * step.  The page gives neither formulas nor thresholds; the readings here:
+ * the statistics of a decode query are its attention entropy (nats) and its
+ * peak probability; the rank of a sequence's current token follows from the
+ * mean over statistic sets and query heads of entropy / ln(n) and from the
+ * largest peak (kvs_router).  A routed rank is applied by encoding the
+ * current token again at that rank (kvs_encode_factorized at its position):
+ * it is the last token of its page, so no later token's codes move.       */
+
+/* kvs_attn_decode on a factorized plan that also writes, per sequence and
+ * query head, the attention statistics:
+ *   stats  device float [batch][Hq][2]: entropy -sum p ln p (nats) and peak
+ *          probability max p of the row's softmax over the keys it saw,
+ *          computed from the same bf16-rounded probabilities as the output;
+ *          (0, 0) for a query that sees no key.
+ * The workspace is that of kvs_attn_decode.  Dense plans ->
+ * KVS_ERR_UNSUPPORTED. */
+KVS_API kvs_status kvs_attn_decode_stats(const kvs_plan* plan, const kvs_cache* cache,
+                                         int32_t layer, const void* q, const int32_t* seq_len,
+                                         int32_t batch, int32_t max_seq_len, int32_t n_splits,
+                                         void* out, int32_t out_dtype, float* stats,
+                                         void* workspace, size_t ws_bytes, void* stream);
+
+typedef struct {
+  float entropy_focused;   /* mean normalized entropy below this: rank_focused  */
+  float entropy_diffuse;   /* at or above this: rank_diffuse; between: rank_mid  */
+  float peak_focused;      /* a peak probability at or above this: rank_focused  */
+  int32_t rank_focused;    /* ranks, clamped to [0, Rmax]                        */
+  int32_t rank_mid;
+  int32_t rank_diffuse;
+} kvs_router;
+
+/* Residual rank of each sequence's current token.
+ *   stats    device float [n_sets][batch][Hq][2] from kvs_attn_decode_stats
+ *            (one set per layer consulted)
+ *   n_keys   device int32 [batch]: keys those queries saw (seq_len, less one
+ *            for a layer with masks_current); h = 0 when n_keys <= 1
+ *   rank_out device uint8 [batch]
+ * h = mean over sets and heads of entropy / ln(n_keys) in fp32, p = the
+ * largest peak; rank = rank_focused if h < entropy_focused or
+ * p >= peak_focused, else rank_mid if h < entropy_diffuse, else
+ * rank_diffuse.  Errors: non-factorized plan -> KVS_ERR_ARG. */
+KVS_API kvs_status kvs_route_ranks(const kvs_plan* plan, const float* stats, int32_t n_sets,
+                                   const int32_t* n_keys, int32_t batch,
+                                   const kvs_router* router, uint8_t* rank_out, void* stream);
+
 /* Description of the last error on this thread ("" if none). */
 KVS_API const char* kvs_last_error(void);
 
