@@ -13,25 +13,38 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "common.cuh"
 #include "internal.h"
 
 namespace kvs {
 namespace {
 
-// one thread per sequence; heads and sets summed in a fixed order
-__global__ __launch_bounds__(64) void route_kernel(RouteLaunch a) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= a.batch) return;
+// one workgroup per sequence: threads take (set, head) entries in a fixed
+// stride, then a fixed-order reduction (wave DPP, then the 4 waves)
+__global__ __launch_bounds__(256) void route_kernel(RouteLaunch a) {
+  __shared__ float part_h[4], part_p[4];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int per_set = a.n_q_heads;
+  const int total = a.n_sets * per_set;
   float hsum = 0.f, peak = 0.f;
-  for (int s = 0; s < a.n_sets; ++s) {
-    const float* row = a.stats + ((size_t)s * a.batch + b) * a.n_q_heads * 2;
-    for (int h = 0; h < a.n_q_heads; ++h) {
-      hsum += row[2 * h];
-      peak = fmaxf(peak, row[2 * h + 1]);
-    }
+  for (int e = tid; e < total; e += 256) {
+    const int s = e / per_set, h = e % per_set;
+    const float* row = a.stats + (((size_t)s * a.batch + b) * a.n_q_heads + h) * 2;
+    hsum += row[0];
+    peak = fmaxf(peak, row[1]);
   }
+  hsum = dev::wave_sum(hsum);
+  peak = dev::wave_max(peak);
+  if ((tid & 63) == 0) {
+    part_h[tid >> 6] = hsum;
+    part_p[tid >> 6] = peak;
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  hsum = (part_h[0] + part_h[1]) + (part_h[2] + part_h[3]);
+  peak = fmaxf(fmaxf(part_p[0], part_p[1]), fmaxf(part_p[2], part_p[3]));
   const int n = a.n_keys[b];
-  const float h = n > 1 ? hsum / ((float)(a.n_sets * a.n_q_heads) * logf((float)n)) : 0.f;
+  const float h = n > 1 ? hsum / ((float)total * logf((float)n)) : 0.f;
   int r;
   if (h < a.entropy_focused || peak >= a.peak_focused)
     r = a.rank_focused;
@@ -45,7 +58,7 @@ __global__ __launch_bounds__(64) void route_kernel(RouteLaunch a) {
 }  // namespace
 
 int launch_route(const RouteLaunch& a, void* stream) {
-  hipLaunchKernelGGL(route_kernel, dim3((a.batch + 63) / 64), dim3(64), 0,
+  hipLaunchKernelGGL(route_kernel, dim3(a.batch), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }

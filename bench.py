@@ -771,6 +771,37 @@ def main():
         res["roofline_two_source"] = {"achieved": b2 / (us2 * 1e-6) / 1e9,
                                       "frac": b2 / (us2 * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                       "bytes_per_launch": b2, "avg_launch_us": us2}
+    if fact:
+        # router statistics: the same cache-flushed launches with the entropy
+        # and peak side output, then the rank choice over every layer's
+        # statistics
+        stats = torch.empty((L, B, wl.n_q_heads, 2), dtype=torch.float32, device="cuda")
+        ev_s = []
+        for _ in range(args.roofline_passes):
+            for l in dom:
+                flush.sum(dim=0)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                K.kvs_attn_decode_stats(plan, cache, l, qs[l], seq_len, wl.ctx, out=outs[l],
+                                        stats=stats[l], n_splits=n_splits, workspace=ws,
+                                        stream=stream)
+                e1.record(stream)
+                ev_s.append((e0, e1))
+        router = K.kvs_router(0.5, 0.8, 0.5, wl.resid_rank_max, wl.resid_rank_max // 2, 0)
+        ranks = torch.empty(B, dtype=torch.uint8, device="cuda")
+        K.kvs_route_ranks(plan, stats, seq_len, router, rank_out=ranks, stream=stream)
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record(stream)
+        for _ in range(10):
+            K.kvs_route_ranks(plan, stats, seq_len, router, rank_out=ranks, stream=stream)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        us_s = sum(e0.elapsed_time(e1) for e0, e1 in ev_s) * 1e3 / len(ev_s)
+        res["router"] = {"decode_with_stats_us": us_s, "decode_us": us,
+                         "stats_overhead_frac": us_s / us - 1.0,
+                         "route_us": r0.elapsed_time(r1) * 1e3 / 10,
+                         "route_sets": L, "routed_ranks": ranks.cpu().tolist()}
     del flush
     calibration_copy()
     traffic = recorded_traffic(wl.name)
