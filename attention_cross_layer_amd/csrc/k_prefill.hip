@@ -50,7 +50,17 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 constexpr int kRows = 32;        // query rows per wave
-constexpr int kVRow = 64 + 8;    // V^T row pitch in keys (16-byte aligned rows)
+constexpr int kVRow = 64 + 8;    // V^T row pitch in keys (144 B: an odd number of 16-byte units)
+
+// Key position inside V^T rows: each 16-key group has its quads 1 and 2
+// swapped, so a lane's 8 keys 16sp + 8(e/4) + 4hh + e%4 (the order of the
+// probabilities in its B operand) are one 16-byte read.
+__device__ __forceinline__ int swz16(int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); }
+// LDS row of dim d in V^T: d with its low 3 bits flipped by bits 3..5, so
+// that the staging writes of 8 consecutive threads (dims 4L + i) and the
+// reads of 8 consecutive lanes (dims 32mb + col) land in 8 different 16-byte
+// bank groups (row pitch 9 units).
+__device__ __forceinline__ int vrow_of(int d) { return d ^ ((d >> 3) & 7); }
 
 struct PrefillParams {
   const uint16_t* k_pool;
@@ -214,14 +224,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
         w[2][u] = v.z & mk;
         w[3][u] = v.w & mk;
       }
-      uint32_t* dst = reinterpret_cast<uint32_t*>(&v_lds[buf][0]);
+      uint16_t* dst = &v_lds[buf][0];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        uint32_t* row = dst + (4 * L + i) * (kVRow / 2) + q * VCH;
+        uint16_t* row = dst + vrow_of(4 * L + i) * kVRow;
+        const int k0 = 2 * VCH * q;                          // first of this thread's keys
+        *reinterpret_cast<uint2*>(row + swz16(k0)) = make_uint2(w[i][0], w[i][1]);
         if constexpr (VCH == 4)
-          *reinterpret_cast<uint4*>(row) = make_uint4(w[i][0], w[i][1], w[i][2], w[i][3]);
-        else
-          *reinterpret_cast<uint2*>(row) = make_uint2(w[i][0], w[i][1]);
+          *reinterpret_cast<uint2*>(row + swz16(k0 + 4)) = make_uint2(w[i][2], w[i][3]);
       }
     }
   };
@@ -310,10 +320,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const int d = 32 * mb + col;
-        const uint16_t* vrow = &v_lds[buf][d * kVRow + 16 * sp + 4 * hh];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-        o[mb] = mfma32(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[sp], o[mb]);
+        const uint16_t* vrow = &v_lds[buf][vrow_of(d) * kVRow + 16 * sp + 8 * hh];
+        o[mb] = mfma32(*reinterpret_cast<const uint4*>(vrow), pb[sp], o[mb]);
       }
   }
 
