@@ -109,6 +109,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
+constexpr float kBumpLog2 = 8.f;                // lazy-maximum slack (log2 units)
 
 // Position of entry j inside its 16-wide group with quads 1 and 2 swapped
 // (an involution; higher bits of j pass through).
@@ -308,6 +309,7 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
 
   f32x16_t acc_c = f32x16_t{}, acc_d = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
+  const float bump_gap = kBumpLog2 / a.scale_log2;   // in raw score units
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
@@ -351,9 +353,15 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m_run, mt);
+    // The reference maximum moves only when a score passes it by more than
+    // kBumpLog2 in log2 units: probabilities stay <= 2^kBumpLog2 (exact
+    // enough in bf16, sums safe in fp32) and the accumulators are rescaled a
+    // few times per row instead of at most tiles.  exp2(scale * (s - m)) is
+    // one fma; a row with no key yet keeps p = 0.
+    const bool bump = mt > m_run + bump_gap;
+    const float mn = bump ? mt : m_run;
     const float neg = mn == -INFINITY ? 0.f : -mn * a.scale_log2;
-    const float alpha = m_run == mn ? 1.f : dev::fast_exp2(fmaf(m_run, a.scale_log2, neg));
+    const float alpha = bump ? dev::fast_exp2(fmaf(m_run, a.scale_log2, neg)) : 1.f;
     m_run = mn;
     float lt = 0.f;
     uint4 pb[4];
