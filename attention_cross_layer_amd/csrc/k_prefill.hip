@@ -219,11 +219,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
       for (int u = 0; u < VCH; ++u) {
         uint4 v = NSRC == 2 ? mix_chunk(vst[0][u], vst[NSRC - 1][u], a.w0, a.w1) : vst[0][u];
         const int k0 = key0 + 2 * (q * VCH + u);                // keys k0, k0+1
-        const uint32_t mk = (page_ok && k0 < T ? 0x0000ffffu : 0u) | (page_ok && k0 + 1 < T ? 0xffff0000u : 0u);
-        w[0][u] = v.x & mk;
-        w[1][u] = v.y & mk;
-        w[2][u] = v.z & mk;
-        w[3][u] = v.w & mk;
+        if (page_ok && key0 + 64 <= T) {                        // whole page in range (uniform)
+          w[0][u] = v.x;
+          w[1][u] = v.y;
+          w[2][u] = v.z;
+          w[3][u] = v.w;
+        } else {
+          const uint32_t mk = (page_ok && k0 < T ? 0x0000ffffu : 0u) | (page_ok && k0 + 1 < T ? 0xffff0000u : 0u);
+          w[0][u] = v.x & mk;
+          w[1][u] = v.y & mk;
+          w[2][u] = v.z & mk;
+          w[3][u] = v.w & mk;
+        }
       }
       uint16_t* dst = &v_lds[buf][0];
 #pragma unroll
