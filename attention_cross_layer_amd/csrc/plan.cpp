@@ -52,6 +52,11 @@ static kvs_status check_config(const kvs_config* c) {
       return fail(KVS_ERR_UNSUPPORTED, "no decode kernel for this dtype/head_dim/group size");
   } else {
     if (c->dtype != KVS_BF16) return fail(KVS_ERR_UNSUPPORTED, "factorized cache is bf16 only");
+    // the factorized kernels address one slot's or layer's pages through
+    // 32-bit buffer offsets (4 KiB of coefficients per page and KV head),
+    // with 2^31 as the out-of-range offset
+    if (pages * c->max_batch * c->n_kv_heads > (int64_t(1) << 19))
+      return fail(KVS_ERR_UNSUPPORTED, "factorized cache too large: max_batch * pages * n_kv_heads must be <= 2^19");
     if (!fact_shape_supported(c->head_dim, group, c->basis_rank, c->resid_rank_max))
       return fail(KVS_ERR_UNSUPPORTED, "no factorized kernel for this head_dim/group/ranks");
   }

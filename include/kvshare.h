@@ -182,7 +182,10 @@ typedef struct {
  * entry only after the reader has run, so the reader's decode query sees
  * positions 0..seq_len-2 and its causal prefill query at position P sees
  * keys 0..P-1 (diagonal masking; a query with no key yields zeros).  KVS_FACTORIZED plans take single
- * sources only: src[l][0] is the layer that writes the pair's coefficients.
+ * sources only: src[l][0] is the layer that writes the pair's coefficients.  A factorized
+ * cache must satisfy max_batch * ceil(max_ctx/64) * n_kv_heads <= 2^19 (its
+ * pools are addressed with 32-bit offsets per slot and layer), else
+ * KVS_ERR_UNSUPPORTED.
  * On success *out receives a plan to release with kvs_plan_free(). */
 KVS_API kvs_status kvs_share_plan(const kvs_config* cfg, const int32_t* src,
                                   const float* w, kvs_plan** out);

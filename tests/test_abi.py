@@ -109,6 +109,16 @@ def test_config_rejections():
     with pytest.raises(K.KvsError) as e:
         K.kvs_share_plan(_cfg(1, B=0), src)
     assert e.value.status == K.KVS_ERR_ARG
+    # factorized pools are addressed with 32-bit offsets per slot / layer:
+    # 64 sequences x 64K tokens x 8 KV heads is the largest accepted size
+    big = K.make_config(2, 32, 8, 128, "bf16", 64, 65536, kind=K.KVS_FACTORIZED, basis_rank=32,
+                        resid_rank_max=16)
+    K.kvs_share_plan(big, torch.tensor([[0, -1], [0, -1]], dtype=torch.int32))
+    bigger = K.make_config(2, 32, 8, 128, "bf16", 65, 65536, kind=K.KVS_FACTORIZED, basis_rank=32,
+                           resid_rank_max=16)
+    with pytest.raises(K.KvsError) as e:
+        K.kvs_share_plan(bigger, torch.tensor([[0, -1], [0, -1]], dtype=torch.int32))
+    assert e.value.status == K.KVS_ERR_UNSUPPORTED
 
 
 def test_cache_layout_sizes():
