@@ -33,7 +33,8 @@ PAGE = 64
 EXPORTS = ("kvs_share_plan", "kvs_plan_free", "kvs_plan_layer", "kvs_plan_summary",
            "kvs_cache_layout", "kvs_decode_splits", "kvs_decode_workspace_size", "kvs_append",
            "kvs_append_factorized", "kvs_encode_workspace_size", "kvs_encode_factorized",
-           "kvs_basis_workspace_size", "kvs_pair_basis", "kvs_residual_basis",
+           "kvs_basis_workspace_size", "kvs_pair_basis", "kvs_pair_bases", "kvs_residual_basis",
+           "kvs_residual_bases",
            "kvs_attn_decode", "kvs_attn_decode_stats", "kvs_route_ranks",
            "kvs_attn_prefill_chunk", "kvs_last_error")
 
@@ -134,6 +135,9 @@ def lib():
         "kvs_attn_decode_stats": (i32, [vp, P(kvs_cache), i32, vp, vp, i32, i32, i32, vp, i32, vp,
                                         vp, sz, vp]),
         "kvs_route_ranks": (i32, [vp, vp, i32, vp, i32, P(kvs_router), vp, vp]),
+        "kvs_pair_bases": (i32, [vp, i32, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]),
+        "kvs_residual_bases": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, sz,
+                                     vp]),
         "kvs_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -361,6 +365,49 @@ def kvs_residual_basis(plan: Plan, k, v, basis_k, basis_v, n_tokens: torch.Tenso
                                     _ptr(basis_k), _ptr(basis_v), _ptr(n_tokens), n, B,
                                     _ptr(ubasis_k), _ptr(ubasis_v), _ptr(workspace),
                                     workspace.numel(), _stream(stream)))
+
+
+def _ptr_array(ts):
+    """Host array of device pointers (None entries -> NULL), or None."""
+    if ts is None:
+        return None
+    arr = (ctypes.c_void_p * len(ts))()
+    for i, t in enumerate(ts):
+        p = _ptr(t)
+        arr[i] = None if p is None else p.value
+    return arr
+
+
+def kvs_pair_bases(plan: Plan, k_a, v_a, k_b, v_b, n_tokens: torch.Tensor, basis_k, basis_v,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvs_pair_basis over lists of pairs (k_b / v_b: None or lists with None
+    entries); the workspace default holds every item at once (at most 32)."""
+    n_items = len(k_a)
+    B, n = k_a[0].shape[0], k_a[0].shape[1]
+    if workspace is None:
+        workspace = torch.empty(kvs_basis_workspace_size(plan, B, n) * min(n_items, 32),
+                                dtype=torch.uint8, device=k_a[0].device)
+    _check(lib().kvs_pair_bases(plan.handle, n_items, _ptr_array(k_a), _ptr_array(v_a),
+                                _ptr_array(k_b), _ptr_array(v_b), _ptr(n_tokens), n, B,
+                                _ptr_array(basis_k), _ptr_array(basis_v), _ptr(workspace),
+                                workspace.numel(), _stream(stream)))
+
+
+def kvs_residual_bases(plan: Plan, k, v, basis_k, basis_v, n_tokens: torch.Tensor, ubasis_k,
+                       ubasis_v, k_owner=None, v_owner=None,
+                       workspace: Optional[torch.Tensor] = None, stream=None):
+    """kvs_residual_basis over lists of layers (k_owner / v_owner: None or
+    lists with None entries for owner layers)."""
+    n_items = len(k)
+    B, n = k[0].shape[0], k[0].shape[1]
+    if workspace is None:
+        workspace = torch.empty(kvs_basis_workspace_size(plan, B, n) * min(n_items, 32),
+                                dtype=torch.uint8, device=k[0].device)
+    _check(lib().kvs_residual_bases(plan.handle, n_items, _ptr_array(k), _ptr_array(v),
+                                    _ptr_array(k_owner), _ptr_array(v_owner), _ptr_array(basis_k),
+                                    _ptr_array(basis_v), _ptr(n_tokens), n, B, _ptr_array(ubasis_k),
+                                    _ptr_array(ubasis_v), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)))
 
 
 def kvs_attn_decode(plan: Plan, cache: Cache, layer: int, q: torch.Tensor,

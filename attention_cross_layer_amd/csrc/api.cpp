@@ -403,10 +403,13 @@ EncodeWs encode_ws(const Plan& p, int32_t batch, int32_t n) {
   return w;
 }
 
-// Basis workspace: Gram matrices [2][Hkv][hd][hd] and eigenvalues [2][Hkv][hd]
-// (fp32), then, for residual directions, the residual rows [2][B][n][Hkv][hd].
+// Basis workspace of one item (K and V of one pair or layer): Gram matrices
+// [2][Hkv][hd][hd] and eigenvalues [2][Hkv][hd] (fp32), and for residual
+// directions the residual rows [2][B][n][Hkv][hd] (fp32).  A batched call
+// lays out the Gram matrices of all its items, then their eigenvalues, then
+// their rows.
 struct BasisWs {
-  size_t gram, evals, rows, total;
+  size_t gram, evals, rows, item;
 };
 BasisWs basis_ws(const Plan& p, int32_t batch, int32_t n) {
   const size_t hd = p.cfg.head_dim, H = p.cfg.n_kv_heads;
@@ -414,7 +417,7 @@ BasisWs basis_ws(const Plan& p, int32_t batch, int32_t n) {
   w.gram = round256(2 * H * hd * hd * 4);
   w.evals = round256(2 * H * hd * 4);
   w.rows = round256((size_t)batch * n * H * hd * 4);
-  w.total = w.gram + w.evals + 2 * w.rows;
+  w.item = w.gram + w.evals + 2 * w.rows;
   return w;
 }
 
@@ -511,29 +514,33 @@ extern "C" kvs_status kvs_basis_workspace_size(const kvs_plan* plan, int32_t bat
   kvs_status st = check_write_side(plan, batch, n);
   if (st != KVS_OK) return st;
   if (!bytes) return fail(KVS_ERR_ARG, "null argument");
-  *bytes = basis_ws(plan->p, batch, n).total;
+  *bytes = basis_ws(plan->p, batch, n).item;
   return KVS_OK;
 }
 
 namespace {
 
-kvs_status check_basis_common(const kvs_plan* plan, const int32_t* n_tokens, int32_t n, int32_t batch,
-                              void* out_k, void* out_v, void* workspace, size_t ws_bytes) {
+// items processed per launch group: as many as the workspace holds, at most
+// kMaxBasisSets / 2
+kvs_status basis_group(const kvs_plan* plan, int32_t n_items, const int32_t* n_tokens, int32_t n,
+                       int32_t batch, void* workspace, size_t ws_bytes, int32_t* group) {
   kvs_status st = check_write_side(plan, batch, n);
   if (st != KVS_OK) return st;
-  if (!n_tokens || !out_k || !out_v || !workspace) return fail(KVS_ERR_ARG, "null argument");
-  if (!aligned4(n_tokens) || !aligned16(out_k) || !aligned16(out_v) || !aligned16(workspace))
-    return fail(KVS_ERR_ALIGN, "outputs and workspace must be 16-byte aligned");
+  if (n_items < 1) return fail(KVS_ERR_ARG, "n_items must be >= 1");
+  if (!n_tokens || !workspace) return fail(KVS_ERR_ARG, "null argument");
+  if (!aligned4(n_tokens) || !aligned16(workspace)) return fail(KVS_ERR_ALIGN, "n_tokens / workspace misaligned");
   const BasisWs w = basis_ws(plan->p, batch, n);
-  if (ws_bytes < w.total) return fail(KVS_ERR_RANGE, "workspace too small: need " + std::to_string(w.total));
+  if (ws_bytes < w.item) return fail(KVS_ERR_RANGE, "workspace too small: need at least " + std::to_string(w.item));
+  *group = (int32_t)std::min<size_t>(ws_bytes / w.item, kMaxBasisSets / 2);
   return KVS_OK;
 }
 
 BasisLaunch basis_launch(const Plan& p, const int32_t* n_tokens, int32_t n, int32_t batch, int32_t k_out,
-                         void* out_k, void* out_v, void* workspace) {
+                         int32_t items, void* workspace) {
   const BasisWs w = basis_ws(p, batch, n);
   char* ws = static_cast<char*>(workspace);
   BasisLaunch b;
+  b.n_sets = 2 * items;
   b.n_tokens = n_tokens;
   b.n = n;
   b.batch = batch;
@@ -541,33 +548,123 @@ BasisLaunch basis_launch(const Plan& p, const int32_t* n_tokens, int32_t n, int3
   b.head_dim = p.cfg.head_dim;
   b.k_out = k_out;
   b.gram = reinterpret_cast<float*>(ws);
-  b.evals = reinterpret_cast<float*>(ws + w.gram);
-  b.out[0] = out_k;
-  b.out[1] = out_v;
+  b.evals = reinterpret_cast<float*>(ws + items * w.gram);
   return b;
 }
 
 }  // namespace
 
+extern "C" kvs_status kvs_pair_bases(const kvs_plan* plan, int32_t n_items, const void* const* k_a,
+                                     const void* const* v_a, const void* const* k_b,
+                                     const void* const* v_b, const int32_t* n_tokens, int32_t n,
+                                     int32_t batch, void* const* basis_k, void* const* basis_v,
+                                     void* workspace, size_t ws_bytes, void* stream) {
+  clear_error();
+  int32_t group = 0;
+  kvs_status st = basis_group(plan, n_items, n_tokens, n, batch, workspace, ws_bytes, &group);
+  if (st != KVS_OK) return st;
+  if (!k_a || !v_a || !basis_k || !basis_v) return fail(KVS_ERR_ARG, "null array");
+  for (int32_t i = 0; i < n_items; ++i) {
+    const void* kb = k_b ? k_b[i] : nullptr;
+    const void* vb = v_b ? v_b[i] : nullptr;
+    if (!k_a[i] || !v_a[i] || !basis_k[i] || !basis_v[i]) return fail(KVS_ERR_ARG, "null argument");
+    if ((kb == nullptr) != (vb == nullptr)) return fail(KVS_ERR_ARG, "give both k_b and v_b, or neither");
+    if (!aligned16(k_a[i]) || !aligned16(v_a[i]) || (kb && (!aligned16(kb) || !aligned16(vb))) ||
+        !aligned16(basis_k[i]) || !aligned16(basis_v[i]))
+      return fail(KVS_ERR_ALIGN, "rows and outputs must be 16-byte aligned");
+  }
+  for (int32_t i0 = 0; i0 < n_items; i0 += group) {
+    const int32_t cnt = std::min(group, n_items - i0);
+    BasisLaunch b = basis_launch(plan->p, n_tokens, n, batch, plan->p.cfg.basis_rank, cnt, workspace);
+    for (int32_t j = 0; j < cnt; ++j) {
+      const int32_t i = i0 + j;
+      b.x[2 * j][0] = k_a[i];
+      b.x[2 * j][1] = k_b ? k_b[i] : nullptr;
+      b.x[2 * j + 1][0] = v_a[i];
+      b.x[2 * j + 1][1] = v_b ? v_b[i] : nullptr;
+      b.out[2 * j] = basis_k[i];
+      b.out[2 * j + 1] = basis_v[i];
+    }
+    b.rows_f32 = 0;
+    if ((st = hip_status(launch_basis(b, stream), "pair basis launch")) != KVS_OK) return st;
+  }
+  return KVS_OK;
+}
+
 extern "C" kvs_status kvs_pair_basis(const kvs_plan* plan, const void* k_a, const void* v_a,
                                      const void* k_b, const void* v_b, const int32_t* n_tokens,
                                      int32_t n, int32_t batch, void* basis_k, void* basis_v,
                                      void* workspace, size_t ws_bytes, void* stream) {
+  return kvs_pair_bases(plan, 1, &k_a, &v_a, &k_b, &v_b, n_tokens, n, batch, &basis_k, &basis_v,
+                        workspace, ws_bytes, stream);
+}
+
+extern "C" kvs_status kvs_residual_bases(const kvs_plan* plan, int32_t n_items, const void* const* k,
+                                         const void* const* v, const void* const* k_owner,
+                                         const void* const* v_owner, const void* const* basis_k,
+                                         const void* const* basis_v, const int32_t* n_tokens,
+                                         int32_t n, int32_t batch, void* const* ubasis_k,
+                                         void* const* ubasis_v, void* workspace, size_t ws_bytes,
+                                         void* stream) {
   clear_error();
-  kvs_status st = check_basis_common(plan, n_tokens, n, batch, basis_k, basis_v, workspace, ws_bytes);
+  int32_t group = 0;
+  kvs_status st = basis_group(plan, n_items, n_tokens, n, batch, workspace, ws_bytes, &group);
   if (st != KVS_OK) return st;
-  if (!k_a || !v_a) return fail(KVS_ERR_ARG, "null argument");
-  if ((k_b == nullptr) != (v_b == nullptr)) return fail(KVS_ERR_ARG, "give both k_b and v_b, or neither");
-  if (!aligned16(k_a) || !aligned16(v_a) || (k_b && (!aligned16(k_b) || !aligned16(v_b))))
-    return fail(KVS_ERR_ALIGN, "rows must be 16-byte aligned");
-  BasisLaunch b = basis_launch(plan->p, n_tokens, n, batch, plan->p.cfg.basis_rank, basis_k, basis_v,
-                               workspace);
-  b.x[0][0] = k_a;
-  b.x[0][1] = k_b;
-  b.x[1][0] = v_a;
-  b.x[1][1] = v_b;
-  b.rows_f32 = 0;
-  return hip_status(launch_basis(b, stream), "pair basis launch");
+  if (!k || !v || !basis_k || !basis_v || !ubasis_k || !ubasis_v) return fail(KVS_ERR_ARG, "null array");
+  for (int32_t i = 0; i < n_items; ++i) {
+    const void* ko = k_owner ? k_owner[i] : nullptr;
+    const void* vo = v_owner ? v_owner[i] : nullptr;
+    if (!k[i] || !v[i] || !basis_k[i] || !basis_v[i] || !ubasis_k[i] || !ubasis_v[i])
+      return fail(KVS_ERR_ARG, "null argument");
+    if ((ko == nullptr) != (vo == nullptr)) return fail(KVS_ERR_ARG, "give both k_owner and v_owner, or neither");
+    if (!aligned16(k[i]) || !aligned16(v[i]) || !aligned16(basis_k[i]) || !aligned16(basis_v[i]) ||
+        !aligned16(ubasis_k[i]) || !aligned16(ubasis_v[i]) || (ko && (!aligned16(ko) || !aligned16(vo))))
+      return fail(KVS_ERR_ALIGN, "rows, bases and outputs must be 16-byte aligned");
+  }
+  const Plan& p = plan->p;
+  const BasisWs w = basis_ws(p, batch, n);
+  char* ws = static_cast<char*>(workspace);
+  for (int32_t i0 = 0; i0 < n_items; i0 += group) {
+    const int32_t cnt = std::min(group, n_items - i0);
+    BasisLaunch b = basis_launch(p, n_tokens, n, batch, p.cfg.resid_rank_max, cnt, workspace);
+    char* rows_base = ws + cnt * (w.gram + w.evals);
+    for (int32_t j = 0; j < cnt; ++j) {
+      const int32_t i = i0 + j;
+      float* rows[2] = {reinterpret_cast<float*>(rows_base + (2 * j) * w.rows),
+                        reinterpret_cast<float*>(rows_base + (2 * j + 1) * w.rows)};
+      EncodeLaunch e;
+      const void* x[2] = {k[i], v[i]};
+      const void* xo[2] = {k_owner && k_owner[i] ? k_owner[i] : k[i], v_owner && v_owner[i] ? v_owner[i] : v[i]};
+      const void* bases[2] = {basis_k[i], basis_v[i]};
+      for (int side = 0; side < 2; ++side) {
+        e.x[side] = x[side];
+        e.xo[side] = xo[side];
+        e.basis[side] = bases[side];
+        e.ubasis[side] = nullptr;
+        e.c_out[side] = nullptr;
+        e.d_out[side] = nullptr;
+        e.s_out[side] = nullptr;
+        e.e_out[side] = rows[side];
+      }
+      e.rank = nullptr;
+      e.n_tokens = n_tokens;
+      e.n = n;
+      e.batch = batch;
+      e.n_kv_heads = p.cfg.n_kv_heads;
+      e.head_dim = p.cfg.head_dim;
+      e.residual_mode = 1;
+      if ((st = hip_status(launch_encode(e, stream), "residual rows launch")) != KVS_OK) return st;
+      b.x[2 * j][0] = rows[0];
+      b.x[2 * j][1] = nullptr;
+      b.x[2 * j + 1][0] = rows[1];
+      b.x[2 * j + 1][1] = nullptr;
+      b.out[2 * j] = ubasis_k[i];
+      b.out[2 * j + 1] = ubasis_v[i];
+    }
+    b.rows_f32 = 1;
+    if ((st = hip_status(launch_basis(b, stream), "residual basis launch")) != KVS_OK) return st;
+  }
+  return KVS_OK;
 }
 
 extern "C" kvs_status kvs_residual_basis(const kvs_plan* plan, const void* k, const void* v,
@@ -576,46 +673,6 @@ extern "C" kvs_status kvs_residual_basis(const kvs_plan* plan, const void* k, co
                                          const int32_t* n_tokens, int32_t n, int32_t batch,
                                          void* ubasis_k, void* ubasis_v, void* workspace,
                                          size_t ws_bytes, void* stream) {
-  clear_error();
-  kvs_status st = check_basis_common(plan, n_tokens, n, batch, ubasis_k, ubasis_v, workspace, ws_bytes);
-  if (st != KVS_OK) return st;
-  if (!k || !v || !basis_k || !basis_v) return fail(KVS_ERR_ARG, "null argument");
-  if ((k_owner == nullptr) != (v_owner == nullptr)) return fail(KVS_ERR_ARG, "give both k_owner and v_owner, or neither");
-  if (!aligned16(k) || !aligned16(v) || !aligned16(basis_k) || !aligned16(basis_v) ||
-      (k_owner && (!aligned16(k_owner) || !aligned16(v_owner))))
-    return fail(KVS_ERR_ALIGN, "rows and bases must be 16-byte aligned");
-  const Plan& p = plan->p;
-  const BasisWs w = basis_ws(p, batch, n);
-  char* ws = static_cast<char*>(workspace);
-  float* rows[2] = {reinterpret_cast<float*>(ws + w.gram + w.evals),
-                    reinterpret_cast<float*>(ws + w.gram + w.evals + w.rows)};
-  EncodeLaunch e;
-  const void* x[2] = {k, v};
-  const void* xo[2] = {k_owner ? k_owner : k, v_owner ? v_owner : v};
-  const void* bases[2] = {basis_k, basis_v};
-  for (int side = 0; side < 2; ++side) {
-    e.x[side] = x[side];
-    e.xo[side] = xo[side];
-    e.basis[side] = bases[side];
-    e.ubasis[side] = nullptr;
-    e.c_out[side] = nullptr;
-    e.d_out[side] = nullptr;
-    e.s_out[side] = nullptr;
-    e.e_out[side] = rows[side];
-  }
-  e.rank = nullptr;
-  e.n_tokens = n_tokens;
-  e.n = n;
-  e.batch = batch;
-  e.n_kv_heads = p.cfg.n_kv_heads;
-  e.head_dim = p.cfg.head_dim;
-  e.residual_mode = 1;
-  if ((st = hip_status(launch_encode(e, stream), "residual rows launch")) != KVS_OK) return st;
-  BasisLaunch b = basis_launch(p, n_tokens, n, batch, p.cfg.resid_rank_max, ubasis_k, ubasis_v, workspace);
-  b.x[0][0] = rows[0];
-  b.x[0][1] = nullptr;
-  b.x[1][0] = rows[1];
-  b.x[1][1] = nullptr;
-  b.rows_f32 = 1;
-  return hip_status(launch_basis(b, stream), "residual basis launch");
+  return kvs_residual_bases(plan, 1, &k, &v, &k_owner, &v_owner, &basis_k, &basis_v, n_tokens, n,
+                            batch, &ubasis_k, &ubasis_v, workspace, ws_bytes, stream);
 }

@@ -232,9 +232,12 @@ struct EncodeLaunch {
 int launch_encode(const EncodeLaunch& a, void* stream);
 bool encode_shape_supported(int32_t head_dim, int32_t basis_rank, int32_t resid_rank_max);
 
-// Basis builder: Gram matrices of the rows, then leading eigenvectors.
+// Basis builder: Gram matrices of the rows, then leading eigenvectors, for
+// up to kMaxBasisSets matrix sets per launch (a set = K or V of one basis).
+constexpr int kMaxBasisSets = 64;
 struct BasisLaunch {
-  const void* x[2][2];         // [side][source] rows, [B][n][Hkv][hd]; source 1 may be null
+  int32_t n_sets;
+  const void* x[kMaxBasisSets][2];   // [set][source] rows, [B][n][Hkv][hd]; source 1 may be null
   int32_t rows_f32;            // rows are fp32 (residual rows) instead of bf16
   const int32_t* n_tokens;     // [B]
   int32_t n;
@@ -242,9 +245,9 @@ struct BasisLaunch {
   int32_t n_kv_heads;
   int32_t head_dim;
   int32_t k_out;
-  float* gram;                 // workspace [2][Hkv][hd][hd]
-  float* evals;                // workspace [2][Hkv][hd]
-  void* out[2];                // [Hkv][k_out][hd] bf16
+  float* gram;                 // workspace [set][Hkv][hd][hd]
+  float* evals;                // workspace [set][Hkv][hd]
+  void* out[kMaxBasisSets];    // [Hkv][k_out][hd] bf16 per set
 };
 int launch_basis(const BasisLaunch& a, void* stream);
 

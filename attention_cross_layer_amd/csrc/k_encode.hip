@@ -230,23 +230,24 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeParams a) {
 // ------------------------------------------------------------ Gram matrices
 
 struct GramParams {
-  const void* x[2][2];      // [side][source] rows ([B][n][Hkv][hd]); x[s][1] may be null
+  const void* x[kMaxBasisSets][2];   // [matrix set][source] rows ([B][n][Hkv][hd]); source 1 may be null
   int32_t rows_f32;         // 1: fp32 rows, 0: bf16 rows
   const int32_t* n_tokens;  // [B]
   int32_t n;
   int32_t batch;
   int32_t n_kv_heads;
-  float* gram;              // [side][Hkv][hd][hd]
+  float* gram;              // [set][Hkv][hd][hd]
 };
 
-// grid (NB (NB+1) / 2 block pairs, Hkv, 2 sides), 256 threads; thread (ti, tj) owns
+// grid (NB (NB+1) / 2 block pairs, Hkv, matrix sets), 256 threads; a set is
+// one of K / V of one basis; thread (ti, tj) owns
 // G[32bi + ti][32bj + 4tj .. +3]
 template <int HD>
 __global__ __launch_bounds__(256) void gram_kernel(GramParams a) {
   constexpr int NB = HD / 32;
   __shared__ float xs[2][64][33];
   const int tid = threadIdx.x;
-  const int h = blockIdx.y, side = blockIdx.z;
+  const int h = blockIdx.y, side = blockIdx.z;   // side: the matrix set
   int pr = blockIdx.x, bi = 0;
   while (pr >= NB - bi) {
     pr -= NB - bi;
@@ -320,15 +321,15 @@ __global__ __launch_bounds__(256) void gram_kernel(GramParams a) {
 // --------------------------------------------------- symmetric eigenvectors
 
 struct EigParams {
-  const float* gram;        // [side][Hkv][hd][hd]
+  const float* gram;        // [set][Hkv][hd][hd]
   int32_t k_out;            // leading eigenvectors to write
   int32_t n_kv_heads;
-  uint16_t* out[2];         // per side [Hkv][k_out][hd] bf16
-  float* evals;             // [side][Hkv][hd] eigenvalues, descending
+  uint16_t* out[kMaxBasisSets];   // per set [Hkv][k_out][hd] bf16
+  float* evals;             // [set][Hkv][hd] eigenvalues, descending
   int32_t max_sweeps;
 };
 
-// one workgroup of 1024 threads per matrix: blockIdx.x = side * Hkv + head.
+// one workgroup of 1024 threads per matrix: blockIdx.x = set * Hkv + head.
 // Each round rotates 64 disjoint index pairs at once: every 2x2 block
 // A[{p_i,q_i}, {p_j,q_j}] becomes J_i^T A J_j (one read and one write of the
 // block), and V's columns p_i, q_i rotate.  A pair is rotated only while its
@@ -478,15 +479,15 @@ int run_encode(const EncodeParams& p, int batch, hipStream_t st) {
 }
 
 template <int HD>
-int run_gram(const GramParams& p, hipStream_t st) {
+int run_gram(const GramParams& p, int n_sets, hipStream_t st) {
   constexpr int NB = HD / 32;
-  hipLaunchKernelGGL(gram_kernel<HD>, dim3(NB * (NB + 1) / 2, p.n_kv_heads, 2), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(gram_kernel<HD>, dim3(NB * (NB + 1) / 2, p.n_kv_heads, n_sets), dim3(256), 0, st, p);
   return (int)hipGetLastError();
 }
 
 template <int HD>
-int run_eig(const EigParams& p, hipStream_t st) {
-  hipLaunchKernelGGL(eig_kernel<HD>, dim3(2 * p.n_kv_heads), dim3(1024), 0, st, p);
+int run_eig(const EigParams& p, int n_sets, hipStream_t st) {
+  hipLaunchKernelGGL(eig_kernel<HD>, dim3(n_sets * p.n_kv_heads), dim3(1024), 0, st, p);
   return (int)hipGetLastError();
 }
 
@@ -522,9 +523,10 @@ int launch_encode(const EncodeLaunch& a, void* stream) {
 
 int launch_basis(const BasisLaunch& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.n_sets < 1 || a.n_sets > kMaxBasisSets) return (int)hipErrorInvalidValue;
   GramParams g;
-  for (int side = 0; side < 2; ++side)
-    for (int src = 0; src < 2; ++src) g.x[side][src] = a.x[side][src];
+  for (int m = 0; m < a.n_sets; ++m)
+    for (int src = 0; src < 2; ++src) g.x[m][src] = a.x[m][src];
   g.rows_f32 = a.rows_f32;
   g.n_tokens = a.n_tokens;
   g.n = a.n;
@@ -535,18 +537,17 @@ int launch_basis(const BasisLaunch& a, void* stream) {
   e.gram = a.gram;
   e.k_out = a.k_out;
   e.n_kv_heads = a.n_kv_heads;
-  e.out[0] = static_cast<uint16_t*>(a.out[0]);
-  e.out[1] = static_cast<uint16_t*>(a.out[1]);
+  for (int m = 0; m < a.n_sets; ++m) e.out[m] = static_cast<uint16_t*>(a.out[m]);
   e.evals = a.evals;
   e.max_sweeps = 20;
   int err;
   if (a.head_dim == 64) {
-    if ((err = run_gram<64>(g, st)) != 0) return err;
-    return run_eig<64>(e, st);
+    if ((err = run_gram<64>(g, a.n_sets, st)) != 0) return err;
+    return run_eig<64>(e, a.n_sets, st);
   }
   if (a.head_dim == 128) {
-    if ((err = run_gram<128>(g, st)) != 0) return err;
-    return run_eig<128>(e, st);
+    if ((err = run_gram<128>(g, a.n_sets, st)) != 0) return err;
+    return run_eig<128>(e, a.n_sets, st);
   }
   return (int)hipErrorInvalidValue;
 }

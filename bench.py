@@ -149,7 +149,6 @@ PREFILL_WORKLOAD = "depthgraft_prefill_chunk"
 FACT_PREFILL_WORKLOAD = "factorized_prefill_chunk"
 PREFILL_WORKLOADS = (PREFILL_WORKLOAD, FACT_PREFILL_WORKLOAD)
 ENCODE_WORKLOAD = "factorized_encode_chunk"
-N_BASIS_STREAMS = 4
 CALIB_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {"decode_kernel": "k_decode.hip", "decode_mfma_kernel": "k_decode.hip",
@@ -525,35 +524,27 @@ def encode_main(args):
     uv = cache.ubasis_v.view(torch.bfloat16).view(wl.n_layers, Hkv, Rm, hd)
     ews = torch.empty(K.kvs_encode_workspace_size(plan, 1, n), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    # the pairs are independent: their bases are built on N_BASIS_STREAMS
-    # streams (default priority), each with its own workspace
-    side = [torch.cuda.Stream() for _ in range(N_BASIS_STREAMS)]
-    bws = [torch.empty(K.kvs_basis_workspace_size(plan, 1, n), dtype=torch.uint8, device="cuda")
-           for _ in side]
+    # every pair's basis in one batched call, then every layer's residual
+    # directions in one batched call, with a workspace that holds all items
+    item = K.kvs_basis_workspace_size(plan, 1, n)
+    bws = torch.empty(item * wl.n_layers, dtype=torch.uint8, device="cuda")
 
     def owner_of(l):
         return int(src[l, 0])
 
     def build_bases():
-        start_ev = torch.cuda.Event()
-        start_ev.record(stream)
-        for st in side:
-            st.wait_event(start_ev)
-        for idx, o in enumerate(owners):
-            st, ws = side[idx % len(side)], bws[idx % len(side)]
-            (ka, va), (kb, vb) = rows[o], rows[o + 1]
-            slot = owners.index(o)
-            K.kvs_pair_basis(plan, ka, va, kb, vb, n_tok, bk[slot], bv[slot], workspace=ws,
-                             stream=st)
-            for l in (o, o + 1):
-                k, v = rows[l]
-                K.kvs_residual_basis(plan, k, v, bk[slot], bv[slot], n_tok, uk[l], uv[l],
-                                     k_owner=None if l == o else ka,
-                                     v_owner=None if l == o else va, workspace=ws, stream=st)
-        for st in side:
-            done_ev = torch.cuda.Event()
-            done_ev.record(st)
-            stream.wait_event(done_ev)
+        K.kvs_pair_bases(plan, [rows[o][0] for o in owners], [rows[o][1] for o in owners],
+                         [rows[o + 1][0] for o in owners], [rows[o + 1][1] for o in owners],
+                         n_tok, [bk[i] for i in range(len(owners))],
+                         [bv[i] for i in range(len(owners))], workspace=bws, stream=stream)
+        L_all = list(range(wl.n_layers))
+        slot = [owners.index(owner_of(l)) for l in L_all]
+        K.kvs_residual_bases(plan, [rows[l][0] for l in L_all], [rows[l][1] for l in L_all],
+                             [bk[slot[l]] for l in L_all], [bv[slot[l]] for l in L_all], n_tok,
+                             [uk[l] for l in L_all], [uv[l] for l in L_all],
+                             k_owner=[None if owner_of(l) == l else rows[owner_of(l)][0] for l in L_all],
+                             v_owner=[None if owner_of(l) == l else rows[owner_of(l)][1] for l in L_all],
+                             workspace=bws, stream=stream)
 
     build_bases()
     torch.cuda.synchronize()
@@ -610,8 +601,7 @@ def encode_main(args):
                         "owner_layer_avg_us": sum(per[l] for l in owners) / len(owners)},
            "basis_build_ms": basis_ms,
            "basis_build": f"{len(owners)} pair bases + {wl.n_layers} residual bases "
-                          f"(K and V) from {n} rows per layer, pairs spread over "
-                          f"{N_BASIS_STREAMS} streams"}
+                          f"(K and V) from {n} rows per layer, two batched calls"}
     print(json.dumps(res), flush=True)
 
 

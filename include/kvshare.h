@@ -286,7 +286,8 @@ KVS_API kvs_status kvs_encode_factorized(const kvs_plan* plan, const kvs_cache* 
                                          const int32_t* start_pos, int32_t batch,
                                          void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes kvs_pair_basis / kvs_residual_basis need for (batch, n). */
+/* Workspace bytes kvs_pair_basis / kvs_residual_basis need for (batch, n):
+ * one basis item (K and V of one pair or layer). */
 KVS_API kvs_status kvs_basis_workspace_size(const kvs_plan* plan, int32_t batch, int32_t n,
                                             size_t* bytes);
 
@@ -302,6 +303,19 @@ KVS_API kvs_status kvs_pair_basis(const kvs_plan* plan, const void* k_a, const v
                                   int32_t n, int32_t batch, void* basis_k, void* basis_v,
                                   void* workspace, size_t ws_bytes, void* stream);
 
+/* kvs_pair_basis for n_items pairs at once: every argument named for one pair
+ * becomes a host array of n_items device pointers (k_b / v_b: NULL, or an
+ * array whose entries may be NULL).  All pairs share n, batch and n_tokens.
+ * The matrices of as many items as the workspace holds
+ * (ws_bytes / kvs_basis_workspace_size, at most 32) are diagonalized in one
+ * launch, so a larger workspace lets more of the GPU work at once; results
+ * equal those of one call per item. */
+KVS_API kvs_status kvs_pair_bases(const kvs_plan* plan, int32_t n_items, const void* const* k_a,
+                                  const void* const* v_a, const void* const* k_b,
+                                  const void* const* v_b, const int32_t* n_tokens, int32_t n,
+                                  int32_t batch, void* const* basis_k, void* const* basis_v,
+                                  void* workspace, size_t ws_bytes, void* stream);
+
 /* Residual directions (UK and UV) of a layer from its rows, the slot owner's
  * rows (NULL when the layer is the owner) and the pair basis (bf16
  * [Hkv][R][hd], as stored).  ubasis_k / ubasis_v: device bf16
@@ -312,6 +326,17 @@ KVS_API kvs_status kvs_residual_basis(const kvs_plan* plan, const void* k, const
                                       const int32_t* n_tokens, int32_t n, int32_t batch,
                                       void* ubasis_k, void* ubasis_v, void* workspace,
                                       size_t ws_bytes, void* stream);
+
+/* kvs_residual_basis for n_items layers at once, in the manner of
+ * kvs_pair_bases (k_owner / v_owner: NULL, or arrays whose entries may be
+ * NULL for owner layers). */
+KVS_API kvs_status kvs_residual_bases(const kvs_plan* plan, int32_t n_items, const void* const* k,
+                                      const void* const* v, const void* const* k_owner,
+                                      const void* const* v_owner, const void* const* basis_k,
+                                      const void* const* basis_v, const int32_t* n_tokens,
+                                      int32_t n, int32_t batch, void* const* ubasis_k,
+                                      void* const* ubasis_v, void* workspace, size_t ws_bytes,
+                                      void* stream);
 
 /* ---------------------------------------------------------------- attention */
 

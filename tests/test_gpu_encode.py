@@ -274,3 +274,62 @@ def test_gpu_chain_decodes_like_the_oracle_chain():
         max_abs, rel = errors(got, A.attend_decode(q, kk, vv, lens))
         note(f"   chain layer {layer}: max_abs {max_abs:.2e} rel {rel:.2e}")
         assert max_abs <= 1e-2 and rel <= 5e-3
+
+
+def test_batched_bases_equal_single_calls():
+    """kvs_pair_bases / kvs_residual_bases over several items (one launch
+    group, and a workspace that forces groups of one) give bit-identical bases
+    to one call per item."""
+    wl = F.with_(n_layers=4, n_q_heads=8, n_kv_heads=2)
+    B, ctx = 1, 200
+    src, w = datagen.share_map(wl)
+    cfg = K.make_config(4, 8, 2, 128, "bf16", B, ctx, kind=K.KVS_FACTORIZED, basis_rank=32,
+                        resid_rank_max=16)
+    plan = K.kvs_share_plan(cfg, src, w)
+    n_tok = torch.tensor([ctx - 9], dtype=torch.int32).cuda()
+    rows = {}
+    for pair in range(2):
+        ka, kb = datagen.correlated_pair_rows(wl, pair, "k", batch=B, ctx=ctx)
+        va, vb = datagen.correlated_pair_rows(wl, pair, "v", batch=B, ctx=ctx)
+        rows[2 * pair], rows[2 * pair + 1] = (ka.cuda(), va.cuda()), (kb.cuda(), vb.cuda())
+
+    def empty(k):
+        return [torch.empty((2, k, 128), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+
+    single = [empty(32) for _ in range(2)]
+    for pair in range(2):
+        (ka, va), (kb, vb) = rows[2 * pair], rows[2 * pair + 1]
+        K.kvs_pair_basis(plan, ka, va, kb, vb, n_tok, single[pair][0], single[pair][1])
+    item = K.kvs_basis_workspace_size(plan, B, ctx)
+    for ws_items in (2, 1):
+        ws = torch.empty(item * ws_items, dtype=torch.uint8, device="cuda")
+        batched = [empty(32) for _ in range(2)]
+        K.kvs_pair_bases(plan, [rows[0][0], rows[2][0]], [rows[0][1], rows[2][1]],
+                         [rows[1][0], rows[3][0]], [rows[1][1], rows[3][1]], n_tok,
+                         [b[0] for b in batched], [b[1] for b in batched], workspace=ws)
+        torch.cuda.synchronize()
+        for pair in range(2):
+            assert torch.equal(batched[pair][0], single[pair][0])
+            assert torch.equal(batched[pair][1], single[pair][1])
+    layers = [0, 1, 3]
+    owner = {0: None, 1: rows[0], 3: rows[2]}
+    single_u = {l: empty(16) for l in layers}
+    for l in layers:
+        slot = l // 2
+        K.kvs_residual_basis(plan, rows[l][0], rows[l][1], single[slot][0], single[slot][1], n_tok,
+                             single_u[l][0], single_u[l][1],
+                             k_owner=None if owner[l] is None else owner[l][0],
+                             v_owner=None if owner[l] is None else owner[l][1])
+    for ws_items in (3, 2):
+        ws = torch.empty(item * ws_items, dtype=torch.uint8, device="cuda")
+        batched_u = {l: empty(16) for l in layers}
+        K.kvs_residual_bases(plan, [rows[l][0] for l in layers], [rows[l][1] for l in layers],
+                             [single[l // 2][0] for l in layers], [single[l // 2][1] for l in layers],
+                             n_tok, [batched_u[l][0] for l in layers], [batched_u[l][1] for l in layers],
+                             k_owner=[None if owner[l] is None else owner[l][0] for l in layers],
+                             v_owner=[None if owner[l] is None else owner[l][1] for l in layers],
+                             workspace=ws)
+        torch.cuda.synchronize()
+        for l in layers:
+            assert torch.equal(batched_u[l][0], single_u[l][0]), (ws_items, l)
+            assert torch.equal(batched_u[l][1], single_u[l][1]), (ws_items, l)
