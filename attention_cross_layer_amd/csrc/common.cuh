@@ -66,6 +66,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// IEEE 754-2019 maximum (a NaN operand gives NaN, -0 < +0).  gfx950 has it as
+// v_maximum3_f32, which needs none of the quieting copies that fmaxf takes
+// under IEEE mode; max3(m, a, b) is one instruction.
+__device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float fmax3_ieee(float m, float a, float b) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(m, a), b);
+}
+
 // Buffer loads through a resource over [base, base + bytes): an offset at or
 // past the end returns zeros and moves no data, so a load that may be absent
 // is issued unconditionally with offset kOOB instead of under a branch.

@@ -351,8 +351,8 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+      for (int r = 0; r < 16; r += 2) mt = dev::fmax3_ieee(mt, s[kb][r], s[kb][r + 1]);
+    mt = dev::fmax_ieee(mt, __shfl_xor(mt, 32));
     // The reference maximum moves only when a score passes it by more than
     // kBumpLog2 in log2 units: probabilities stay <= 2^kBumpLog2 (exact
     // enough in bf16, sums safe in fp32) and the accumulators are rescaled a

@@ -217,29 +217,33 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
       uint32_t w[4][VCH];
 #pragma unroll
       for (int u = 0; u < VCH; ++u) {
-        uint4 v = NSRC == 2 ? mix_chunk(vst[0][u], vst[NSRC - 1][u], a.w0, a.w1) : vst[0][u];
-        const int k0 = key0 + 2 * (q * VCH + u);                // keys k0, k0+1
-        if (page_ok && key0 + 64 <= T) {                        // whole page in range (uniform)
-          w[0][u] = v.x;
-          w[1][u] = v.y;
-          w[2][u] = v.z;
-          w[3][u] = v.w;
-        } else {
+        const uint4 v = NSRC == 2 ? mix_chunk(vst[0][u], vst[NSRC - 1][u], a.w0, a.w1) : vst[0][u];
+        w[0][u] = v.x;
+        w[1][u] = v.y;
+        w[2][u] = v.z;
+        w[3][u] = v.w;
+      }
+      if (!(page_ok && key0 + 64 <= T)) {                       // a page not wholly in range (uniform)
+#pragma unroll
+        for (int u = 0; u < VCH; ++u) {
+          const int k0 = key0 + 2 * (q * VCH + u);              // keys k0, k0+1
           const uint32_t mk = (page_ok && k0 < T ? 0x0000ffffu : 0u) | (page_ok && k0 + 1 < T ? 0xffff0000u : 0u);
-          w[0][u] = v.x & mk;
-          w[1][u] = v.y & mk;
-          w[2][u] = v.z & mk;
-          w[3][u] = v.w & mk;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i][u] &= mk;
         }
       }
+      // one dword store per (dim row, key pair); pairs in key order, each
+      // group of two at swz16 of its first key
       uint16_t* dst = &v_lds[buf][0];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        uint16_t* row = dst + vrow_of(4 * L + i) * kVRow;
+        uint32_t* row = reinterpret_cast<uint32_t*>(dst + vrow_of(4 * L + i) * kVRow);
         const int k0 = 2 * VCH * q;                          // first of this thread's keys
-        *reinterpret_cast<uint2*>(row + swz16(k0)) = make_uint2(w[i][0], w[i][1]);
-        if constexpr (VCH == 4)
-          *reinterpret_cast<uint2*>(row + swz16(k0 + 4)) = make_uint2(w[i][2], w[i][3]);
+#pragma unroll
+        for (int u = 0; u < VCH; u += 2) {
+          row[swz16(k0 + 2 * u) / 2] = w[i][u];
+          row[swz16(k0 + 2 * u) / 2 + 1] = w[i][u + 1];
+        }
       }
     }
   };
@@ -287,8 +291,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[kb][r], s[kb][r + 1]));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+      for (int r = 0; r < 16; r += 2) mt = dev::fmax3_ieee(mt, s[kb][r], s[kb][r + 1]);
+    mt = dev::fmax_ieee(mt, __shfl_xor(mt, 32));
     // The reference maximum moves only when a score passes it by more than
     // kBumpLog2 in log2 units: probabilities stay <= 2^kBumpLog2 (exact
     // enough in bf16, sums safe in fp32) and the accumulators are rescaled a
