@@ -199,8 +199,7 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
     const int ph = pt[t];
     return (unsigned)ph < P ? ph : -1;
   };
-  auto load_meta = [&](int t) -> uint32_t {
-    const int ph = phys_of(t);
+  auto load_meta = [&](int t, int ph) -> uint32_t {
     const bool on = ph >= 0 && t * 64 + skey < T;
     return ld2(r_meta, on ? ((uint32_t)ph * kPage + skey) * 2 : kOOB);
   };
@@ -208,8 +207,7 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
   uint4 ck_r, cv_r;
   uint32_t dk_r, dv_r, sk_r, sv_r;
   int ph_r;
-  auto load_tile = [&](int t, uint32_t meta) {
-    const int ph = phys_of(t);
+  auto load_tile = [&](int t, int ph, uint32_t meta) {
     ph_r = ph;
     const uint32_t page_kv = (uint32_t)ph * H + kvh;
     const uint32_t cb = ph >= 0 ? page_kv * (kPage * kR * 2) + tid * 16 : kOOB;
@@ -275,13 +273,14 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
     }
   };
 
-  // ---- first page's requests, then the query contraction with the bases
-  uint32_t meta_next = load_meta(0);
+  // ---- first page's requests, then the query contraction with the bases.
+  // Physical pages are looked up a tile before the loads that need them.
+  int ph_a = phys_of(1), ph_b = phys_of(2);   // tiles t + 1 and t + 2 of the loop
   {
-    const uint32_t m0 = meta_next;
-    load_tile(0, m0);
+    const int ph0 = phys_of(0);
+    load_tile(0, ph0, load_meta(0, ph0));
   }
-  meta_next = load_meta(1);
+  uint32_t meta_next = load_meta(1, ph_a);
 
   uint4 bq[2], bu;
   {
@@ -313,12 +312,15 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
+    const int ph_c = phys_of(t + 3);
     store_tile(t, buf);
     {
       const uint32_t m1 = meta_next;
-      load_tile(t + 1, m1);                 // absent past the last tile
+      load_tile(t + 1, ph_a, m1);           // absent past the last tile
     }
-    meta_next = load_meta(t + 2);
+    meta_next = load_meta(t + 2, ph_b);
+    ph_a = ph_b;
+    ph_b = ph_c;
     __syncthreads();
     const uint16_t* base = lds + buf * kTile;
 

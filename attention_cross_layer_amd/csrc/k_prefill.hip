@@ -182,9 +182,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
   // V chunk u of this thread: key pair (tid / (HD/4)) * VCH + u, dims
   // 4 * (tid % (HD/4)) .. +3 (16-byte unit pair * HD/4 + dim group)
   auto v_chunk = [&](int u) { return ((tid / (HD / 4)) * VCH + u) * (HD / 4) + tid % (HD / 4); };
-  auto load_tile = [&](int t) {
-    int page = pt[t];
-    if ((unsigned)page >= (unsigned)a.n_phys_pages) page = 0;   // corrupt entry: read page 0, masked below
+  auto load_tile = [&](int entry) {
+    const int page = (unsigned)entry < (unsigned)a.n_phys_pages ? entry : 0;   // corrupt entry: read page 0, masked below
     const int64_t tile = ((int64_t)page * a.n_kv_heads + kvh) * (64 * HD);
 #pragma unroll
     for (int s = 0; s < NSRC; ++s) {
@@ -196,9 +195,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
       for (int u = 0; u < VCH; ++u) vst[s][u] = *reinterpret_cast<const uint4*>(vp + v_chunk(u) * 8);
     }
   };
-  auto store_tile = [&](int t, int buf) {
+  auto store_tile = [&](int t, int entry, int buf) {
     const int key0 = t * 64;
-    const bool page_ok = (unsigned)pt[t] < (unsigned)a.n_phys_pages;
+    const bool page_ok = (unsigned)entry < (unsigned)a.n_phys_pages;
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
       // cache layout chunk index -> (key, chunk)
@@ -254,11 +253,18 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float bump_gap = kBumpLog2 / a.scale_log2;   // in raw score units
 
-  if (n_tiles > 0) load_tile(0);
+  // page-table entries of tiles t and t + 1, read a tile ahead of their use
+  // so that no scalar load sits between the tile's staging steps
+  int pt_cur = n_tiles > 0 ? pt[0] : 0;
+  int pt_next = n_tiles > 1 ? pt[1] : 0;
+  if (n_tiles > 0) load_tile(pt_cur);
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    store_tile(t, buf);
-    if (t + 1 < n_tiles) load_tile(t + 1);
+    const int pt_after = pt[min(t + 2, n_tiles - 1)];
+    store_tile(t, pt_cur, buf);
+    if (t + 1 < n_tiles) load_tile(pt_next);
+    pt_cur = pt_next;
+    pt_next = pt_after;
     __syncthreads();
 
     // ---- S^T = K Q^T: two 32-key blocks
@@ -274,6 +280,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
         s[kb] = mfma32(kv, qreg[ks], s[kb]);
       }
     }
+    // the K operand reads run four ahead of the MFMAs that take them
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * KS - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
     // ---- online softmax for this lane's query row, on raw scores (the
     // positive scale commutes with the max); keys past the row's limit are
