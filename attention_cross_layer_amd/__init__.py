@@ -419,7 +419,8 @@ def kvs_attn_decode(plan: Plan, cache: Cache, layer: int, q: torch.Tensor,
     if n_splits == 0:
         n_splits = kvs_decode_splits(plan, B, max_seq_len)
     if workspace is None:
-        # zero-filled: the library's per-(sequence, KV head) counters start at zero
+        # partial results: every partition writes its whole row, so no clearing is
+        # needed; zero-filled only so that a failed launch leaves no stale data
         workspace = torch.zeros(kvs_decode_workspace_size(plan, B, n_splits), dtype=torch.uint8,
                                 device=q.device)
     if out is None:

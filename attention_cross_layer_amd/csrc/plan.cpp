@@ -170,25 +170,41 @@ extern "C" kvs_status kvs_cache_layout(const kvs_plan* plan, kvs_cache_sizes* ou
 }
 
 // Split-K choice.  A decode launch has one 4-wave workgroup per (partition,
-// KV head, sequence).  Aim for kTargetGroups workgroups (one per CU on the
-// 256-CU MI355X) while keeping at least 4 pages (one per wave) per
-// partition; at most max_decode_splits() partitions (the merge keeps one
-// weight per partition in LDS).  One workgroup per CU measured fastest: with
-// S = 1 the second (merge) launch disappears as well.
-static const int32_t kTargetGroups = 256;
+// KV head, sequence), and at least 4 pages (one per wave) per partition, at
+// most max_decode_splits() partitions.  Targets, from split sweeps on one
+// MI355X (cache flushed before each call):
+//  * the factorized kernel and the hd-64 bf16 MFMA kernel: one workgroup per
+//    CU (256); with S = 1 the merge launch disappears as well;
+//  * the VALU kernel (hd 128, fp32, two sources): one per CU when a call
+//    streams more than 384 MB, else four per CU (1024) with S <= 32: small
+//    calls are latency-bound and gain from more waves in flight (DepthGraft's
+//    8 x 8K batch: 70 -> 60 us per single-source layer), large ones lose.
+static const int32_t kGroupsPerCu1 = 256;
+static const int32_t kGroupsPerCu4 = 1024;
+static const double kSmallCallBytes = 384.0 * (1 << 20);
 
 extern "C" kvs_status kvs_decode_splits(const kvs_plan* plan, int32_t batch, int32_t max_seq_len,
                                         int32_t* n_splits) {
   clear_error();
   if (!plan || !n_splits) return fail(KVS_ERR_ARG, "null argument");
   if (batch < 1 || batch > plan->p.cfg.max_batch) return fail(KVS_ERR_RANGE, "batch out of range");
-  int32_t seq = max_seq_len < 1 ? 1 : (max_seq_len > plan->p.cfg.max_ctx ? plan->p.cfg.max_ctx : max_seq_len);
+  const kvs_config& c = plan->p.cfg;
+  int32_t seq = max_seq_len < 1 ? 1 : (max_seq_len > c.max_ctx ? c.max_ctx : max_seq_len);
   const int32_t pages = (seq + kPage - 1) / kPage;
-  const int32_t groups = batch * plan->p.cfg.n_kv_heads;
-  int32_t s = (kTargetGroups + groups - 1) / groups;
+  const int32_t groups = batch * c.n_kv_heads;
+  const bool mfma_kernel = c.dtype == KVS_BF16 && c.head_dim == 64 && c.n_q_heads / c.n_kv_heads <= 16;
+  int32_t target = kGroupsPerCu1, s_max = max_decode_splits();
+  if (c.kind == KVS_DENSE && !mfma_kernel) {
+    const double call_bytes = double(groups) * pages * kPage * c.head_dim * 2 * elem_bytes(c.dtype);
+    if (call_bytes <= kSmallCallBytes) {
+      target = kGroupsPerCu4;
+      s_max = 32;
+    }
+  }
+  int32_t s = (target + groups - 1) / groups;
   const int32_t cap = pages / 4;
   if (s > cap) s = cap;
-  if (s > max_decode_splits()) s = max_decode_splits();
+  if (s > s_max) s = s_max;
   if (s < 1) s = 1;
   *n_splits = s;
   return KVS_OK;

@@ -196,9 +196,11 @@ KVS_API kvs_status kvs_plan_summary(const kvs_plan* plan, kvs_plan_info* out);
 KVS_API kvs_status kvs_cache_layout(const kvs_plan* plan, kvs_cache_sizes* out);
 
 /* Split-K partitions per (sequence, KV head) the decode uses when n_splits=0
- * is passed to kvs_attn_decode: chosen from batch, KV heads and the longest
- * sequence so the launch fills the GPU; partition boundaries fall on 64-key
- * page boundaries. */
+ * is passed to kvs_attn_decode: chosen from batch, KV heads, the longest
+ * sequence and the plan's decode kernel so the launch fills the GPU (one
+ * 4-wave workgroup per CU, or four per CU for calls of the VALU kernel that
+ * stream at most 384 MB); at least 4 pages per partition, at most 64
+ * partitions; partition boundaries fall on 64-key page boundaries. */
 KVS_API kvs_status kvs_decode_splits(const kvs_plan* plan, int32_t batch,
                                      int32_t max_seq_len, int32_t* n_splits);
 /* Workspace bytes kvs_attn_decode needs for (batch, n_splits), n_splits in

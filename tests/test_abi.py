@@ -151,6 +151,23 @@ def test_decode_split_choice_and_workspace():
         K.kvs_decode_splits(plan, 5, 100)
 
 
+def test_decode_split_rule_by_kernel_and_call_size():
+    # VALU kernel (hd 128): a call streaming 1 GiB keeps one workgroup per CU
+    # (4 x 8 x 8 = 256), one of 256 MiB takes four per CU (8 x 8 x 16 = 1024)
+    src, w = datagen.share_map(datagen.WORKLOADS["cla2_64k"])
+    plan = K.kvs_share_plan(_cfg(32, 32, 8, 128, "bf16", 8, 65536), src, w)
+    assert K.kvs_decode_splits(plan, 4, 65536) == 8
+    assert K.kvs_decode_splits(plan, 8, 8192) == 16
+    # at most 32 partitions on the small-call path, at least 4 pages each
+    assert K.kvs_decode_splits(plan, 1, 65536) == 32
+    assert K.kvs_decode_splits(plan, 8, 512) == 2
+    # hd-64 bf16 MFMA kernel: one workgroup per CU
+    src, w = datagen.share_map(datagen.WORKLOADS["tinyllama_cla2"])
+    plan = K.kvs_share_plan(_cfg(22, 32, 4, 64, "bf16", 64, 2048), src, w)
+    assert K.kvs_decode_splits(plan, 64, 2048) == 1
+    assert K.kvs_decode_splits(plan, 16, 8192) == 4
+
+
 class _FakeCache:
     """kvs_cache struct holding aligned non-null fake device addresses; only
     used on calls that must fail validation before any device access."""
