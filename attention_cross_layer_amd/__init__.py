@@ -36,7 +36,7 @@ EXPORTS = ("kvs_share_plan", "kvs_plan_free", "kvs_plan_layer", "kvs_plan_summar
            "kvs_basis_workspace_size", "kvs_pair_basis", "kvs_pair_bases", "kvs_residual_basis",
            "kvs_residual_bases",
            "kvs_attn_decode", "kvs_attn_decode_stats", "kvs_route_ranks",
-           "kvs_attn_prefill_chunk", "kvs_last_error")
+           "kvs_attn_prefill_chunk", "kvs_time_next_launch", "kvs_last_error")
 
 
 class KvsError(RuntimeError):
@@ -138,6 +138,7 @@ def lib():
         "kvs_pair_bases": (i32, [vp, i32, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, sz, vp]),
         "kvs_residual_bases": (i32, [vp, i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, sz,
                                      vp]),
+        "kvs_time_next_launch": (i32, [vp, vp]),
         "kvs_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -468,6 +469,22 @@ def kvs_route_ranks(plan: Plan, stats: torch.Tensor, n_keys: torch.Tensor, route
     _check(lib().kvs_route_ranks(plan.handle, _ptr(st), n_sets, _ptr(n_keys), B,
                                  ctypes.byref(router), _ptr(rank_out), _stream(stream)))
     return rank_out
+
+
+def _event_handle(ev, stream) -> Optional[int]:
+    if ev is None:
+        return None
+    if not ev.cuda_event:            # torch creates the event on its first record
+        ev.record(stream)
+    return ev.cuda_event
+
+
+def kvs_time_next_launch(start, stop, stream=None) -> None:
+    """Time the main kernel of this thread's next attention call with two
+    torch.cuda.Event objects (created with enable_timing=True): start.elapsed_time(stop)
+    is then that kernel's duration.  None, None disarms."""
+    s = stream if stream is not None else torch.cuda.current_stream()
+    _check(lib().kvs_time_next_launch(_event_handle(start, s), _event_handle(stop, s)))
 
 
 def kvs_attn_prefill_chunk(plan: Plan, cache: Cache, layer: int, q: torch.Tensor,

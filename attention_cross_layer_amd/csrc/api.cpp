@@ -26,6 +26,9 @@ kvs_status check_batch(const kvs_plan* plan, int32_t batch) {
   return KVS_OK;
 }
 
+// events armed by kvs_time_next_launch for this thread's next attention call
+thread_local KernelEvents g_next_events;
+
 kvs_status hip_status(int err, const char* what) {
   if (err == 0) return KVS_OK;
   return fail(KVS_ERR_HIP, std::string(what) + ": " + hip_error_name(err));
@@ -79,6 +82,7 @@ kvs_status decode_impl(const kvs_plan* plan, const kvs_cache* cache, int32_t lay
                        const int32_t* seq_len, int32_t batch, int32_t max_seq_len, int32_t n_splits,
                        void* out, int32_t out_dtype, float* stats, void* workspace, size_t ws_bytes,
                        void* stream) {
+  const KernelEvents ev = take_kernel_events();
   kvs_status st = check_layer(plan, layer);
   if (st != KVS_OK) return st;
   const Plan& p = plan->p;
@@ -106,6 +110,7 @@ kvs_status decode_impl(const kvs_plan* plan, const kvs_cache* cache, int32_t lay
         !aligned16(cache->sv_pool) || !aligned16(cache->rank_pool) || !aligned4(cache->page_table))
       return fail(KVS_ERR_ALIGN, "factorized buffers must be 16-byte aligned");
     FactDecodeLaunch f;
+    f.ev = ev;
     f.ck_pool = cache->ck_pool;
     f.cv_pool = cache->cv_pool;
     f.dk_pool = cache->dk_pool;
@@ -145,6 +150,7 @@ kvs_status decode_impl(const kvs_plan* plan, const kvs_cache* cache, int32_t lay
   if (!aligned16(cache->k_pool) || !aligned16(cache->v_pool) || !aligned4(cache->page_table))
     return fail(KVS_ERR_ALIGN, "pools must be 16-byte aligned");
   DecodeLaunch a;
+  a.ev = ev;
   a.k_pool = cache->k_pool;
   a.v_pool = cache->v_pool;
   a.page_table = cache->page_table;
@@ -234,6 +240,7 @@ extern "C" kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cac
                                              const int32_t* seq_len, int32_t batch, int32_t causal,
                                              void* out, int32_t out_dtype, void* stream) {
   clear_error();
+  const KernelEvents ev = take_kernel_events();
   kvs_status st = check_layer(plan, layer);
   if (st != KVS_OK) return st;
   const Plan& p = plan->p;
@@ -257,6 +264,7 @@ extern "C" kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cac
         !aligned16(cache->rank_pool) || !aligned4(cache->page_table))
       return fail(KVS_ERR_ALIGN, "q, out and the factorized buffers must be 16-byte aligned");
     FactPrefillLaunch f;
+    f.ev = ev;
     f.ck_pool = cache->ck_pool;
     f.cv_pool = cache->cv_pool;
     f.dk_pool = cache->dk_pool;
@@ -297,6 +305,7 @@ extern "C" kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cac
       !aligned4(seq_len) || !aligned4(cache->page_table))
     return fail(KVS_ERR_ALIGN, "q, out and the pools must be 16-byte aligned");
   PrefillLaunch a;
+  a.ev = ev;
   a.k_pool = cache->k_pool;
   a.v_pool = cache->v_pool;
   a.page_table = cache->page_table;
@@ -675,4 +684,19 @@ extern "C" kvs_status kvs_residual_basis(const kvs_plan* plan, const void* k, co
                                          size_t ws_bytes, void* stream) {
   return kvs_residual_bases(plan, 1, &k, &v, &k_owner, &v_owner, &basis_k, &basis_v, n_tokens, n,
                             batch, &ubasis_k, &ubasis_v, workspace, ws_bytes, stream);
+}
+
+namespace kvs {
+KernelEvents take_kernel_events() {
+  const KernelEvents ev = g_next_events;
+  g_next_events = KernelEvents{};
+  return ev;
+}
+}  // namespace kvs
+
+extern "C" kvs_status kvs_time_next_launch(void* start_event, void* stop_event) {
+  clear_error();
+  g_next_events.start = start_event;
+  g_next_events.stop = stop_event;
+  return KVS_OK;
 }

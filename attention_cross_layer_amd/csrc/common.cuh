@@ -2,10 +2,27 @@
 // products, wave64 reductions over DPP.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
+
 namespace kvs {
+
+// Launch of a main attention kernel: with the caller's timing events
+// attached (hipExtLaunchKernel records them at the kernel's start and end)
+// when kvs_time_next_launch armed them, else a plain launch.
+template <typename F, typename... Args>
+inline void launch_main(const KernelEvents& ev, F kernel, dim3 grid, dim3 block, hipStream_t st,
+                        Args... args) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, static_cast<hipEvent_t>(ev.start),
+                          static_cast<hipEvent_t>(ev.stop), 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
+
 namespace dev {
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;

@@ -49,6 +49,15 @@ int max_decode_splits();
 // ------------------------------------------------------------ HIP launchers
 // Implemented in the .hip files; each returns a hipError_t value (0 = ok).
 
+// hipEvent_t pair a launcher attaches to its main kernel (hipExtLaunchKernel:
+// start and end of that kernel's execution); both null: a plain launch.
+struct KernelEvents {
+  void* start = nullptr;
+  void* stop = nullptr;
+};
+// The events kvs_time_next_launch armed on this thread, cleared by the call.
+KernelEvents take_kernel_events();
+
 struct DecodeLaunch {
   const void* k_pool;          // base of the K pool
   const void* v_pool;
@@ -74,6 +83,7 @@ struct DecodeLaunch {
   float* ws;                   // workspace base
   void* out;
   int32_t out_dtype;
+  KernelEvents ev;             // on the split-K partition kernel
 };
 int launch_decode(const DecodeLaunch& a, void* stream);
 
@@ -121,6 +131,7 @@ struct PrefillLaunch {
   float scale_log2;
   void* out;
   int32_t out_dtype;
+  KernelEvents ev;
 };
 int launch_prefill(const PrefillLaunch& a, void* stream);
 
@@ -176,6 +187,7 @@ struct FactDecodeLaunch {
   void* out;
   int32_t out_dtype;
   float* stats;                // [B][Hq][2] entropy, peak probability; or null
+  KernelEvents ev;             // on the split-K partition kernel
 };
 int launch_fact_decode(const FactDecodeLaunch& a, void* stream);
 bool fact_shape_supported(int32_t head_dim, int32_t group, int32_t basis_rank,
@@ -206,6 +218,7 @@ struct FactPrefillLaunch {
   float scale_log2;
   void* out;
   int32_t out_dtype;
+  KernelEvents ev;
 };
 int launch_fact_prefill(const FactPrefillLaunch& a, void* stream);
 bool fact_prefill_shape_supported(int32_t head_dim, int32_t group, int32_t basis_rank,

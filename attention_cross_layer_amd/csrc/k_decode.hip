@@ -705,9 +705,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams a) {
 }
 
 template <int G>
-int run_decode_mfma(const DecodeParams& p, int B, hipStream_t st) {
+int run_decode_mfma(const DecodeParams& p, int B, hipStream_t st, const KernelEvents& ev) {
   dim3 grid(p.n_splits, p.n_kv_heads, B);
-  hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(256), 0, st, p);
+  launch_main(ev, decode_mfma_kernel<G>, grid, dim3(256), st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return (int)e;
   hipLaunchKernelGGL((decode_merge_kernel<G, 64>), dim3(p.n_kv_heads, B), dim3(256), 0, st, p);
@@ -715,17 +715,17 @@ int run_decode_mfma(const DecodeParams& p, int B, hipStream_t st) {
 }
 
 template <typename T, int HD, int G, int NSRC>
-int run_decode(const DecodeParams& p, int B, hipStream_t st) {
-  if constexpr (sizeof(T) == 2 && HD == 64 && NSRC == 1 && G <= 16) return run_decode_mfma<G>(p, B, st);
+int run_decode(const DecodeParams& p, int B, hipStream_t st, const KernelEvents& ev) {
+  if constexpr (sizeof(T) == 2 && HD == 64 && NSRC == 1 && G <= 16) return run_decode_mfma<G>(p, B, st, ev);
   dim3 grid(p.n_splits, p.n_kv_heads, B);
-  hipLaunchKernelGGL((decode_kernel<T, HD, G, NSRC>), grid, dim3(256), 0, st, p);
+  launch_main(ev, decode_kernel<T, HD, G, NSRC>, grid, dim3(256), st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return (int)e;
   hipLaunchKernelGGL((decode_merge_kernel<G, HD>), dim3(p.n_kv_heads, B), dim3(256), 0, st, p);
   return (int)hipGetLastError();
 }
 
-typedef int (*DecodeFn)(const DecodeParams&, int, hipStream_t);
+typedef int (*DecodeFn)(const DecodeParams&, int, hipStream_t, const KernelEvents&);
 
 template <typename T, int HD, int NSRC>
 DecodeFn pick_group(int G) {
@@ -793,7 +793,7 @@ int launch_decode(const DecodeLaunch& a, void* stream) {
   p.ws_l = p.ws_m + rows;
   p.out = a.out;
   p.out_bf16 = a.out_dtype == KVS_BF16;
-  return fn(p, a.batch, static_cast<hipStream_t>(stream));
+  return fn(p, a.batch, static_cast<hipStream_t>(stream), a.ev);
 }
 
 const char* hip_error_name(int err) { return hipGetErrorString((hipError_t)err); }

@@ -469,17 +469,17 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
 }
 
 template <int HD, int G>
-int run_fact_prefill(FactPrefillParams p, int B, hipStream_t st) {
+int run_fact_prefill(FactPrefillParams p, int B, hipStream_t st, const KernelEvents& ev) {
   constexpr int HW = G < 4 ? G : 4;
   constexpr int PB = 4 / HW;
   p.head_groups = G / HW;
   p.n_pos_groups = (p.n + PB * kRows - 1) / (PB * kRows);
   dim3 grid(p.n_pos_groups * p.head_groups * p.n_kv_heads, B);
-  hipLaunchKernelGGL((fact_prefill_kernel<HD, G>), grid, dim3(256), 0, st, p);
+  launch_main(ev, fact_prefill_kernel<HD, G>, grid, dim3(256), st, p);
   return (int)hipGetLastError();
 }
 
-typedef int (*FactPrefillFn)(FactPrefillParams, int, hipStream_t);
+typedef int (*FactPrefillFn)(FactPrefillParams, int, hipStream_t, const KernelEvents&);
 
 template <int HD>
 FactPrefillFn pick_g(int G) {
@@ -535,7 +535,7 @@ int launch_fact_prefill(const FactPrefillLaunch& a, void* stream) {
   p.scale_log2 = a.scale_log2;
   p.out = a.out;
   p.out_bf16 = a.out_dtype == KVS_BF16;
-  return fn(p, a.batch, static_cast<hipStream_t>(stream));
+  return fn(p, a.batch, static_cast<hipStream_t>(stream), a.ev);
 }
 
 }  // namespace kvs

@@ -649,9 +649,8 @@ __global__ __launch_bounds__(256) void fact_merge_kernel(FactParams a) {
 }
 
 template <int HD, int G, bool STATS>
-int run_fact_t(const FactParams& p, int B, hipStream_t st) {
-  hipLaunchKernelGGL((fact_decode_kernel<HD, G, STATS>), dim3(p.n_splits, p.n_kv_heads, B), dim3(256),
-                     0, st, p);
+int run_fact_t(const FactParams& p, int B, hipStream_t st, const KernelEvents& ev) {
+  launch_main(ev, fact_decode_kernel<HD, G, STATS>, dim3(p.n_splits, p.n_kv_heads, B), dim3(256), st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return (int)e;
   hipLaunchKernelGGL((fact_merge_kernel<HD, G, STATS>), dim3(p.n_kv_heads, B), dim3(256), 0, st, p);
@@ -659,11 +658,11 @@ int run_fact_t(const FactParams& p, int B, hipStream_t st) {
 }
 
 template <int HD, int G>
-int run_fact(const FactParams& p, int B, hipStream_t st) {
-  return p.stats ? run_fact_t<HD, G, true>(p, B, st) : run_fact_t<HD, G, false>(p, B, st);
+int run_fact(const FactParams& p, int B, hipStream_t st, const KernelEvents& ev) {
+  return p.stats ? run_fact_t<HD, G, true>(p, B, st, ev) : run_fact_t<HD, G, false>(p, B, st, ev);
 }
 
-typedef int (*FactFn)(const FactParams&, int, hipStream_t);
+typedef int (*FactFn)(const FactParams&, int, hipStream_t, const KernelEvents&);
 
 FactFn pick(int hd, int G) {
   if (hd == 64) {
@@ -803,7 +802,7 @@ int launch_fact_decode(const FactDecodeLaunch& a, void* stream) {
   p.stats = a.stats;
   p.out = a.out;
   p.out_bf16 = a.out_dtype == KVS_BF16;
-  return fn(p, a.batch, static_cast<hipStream_t>(stream));
+  return fn(p, a.batch, static_cast<hipStream_t>(stream), a.ev);
 }
 
 int launch_fact_append(const FactAppendLaunch& a, void* stream) {

@@ -16,11 +16,13 @@ synthetic N(0,1) tensors of the workload's shapes.
 Prints one JSON line.  ``value`` is decode tokens/s (one token per sequence
 per step, warm back-to-back steps).  ``roofline`` rates the decode launch of
 a single-source layer against the 8 TB/s HBM peak with its algorithmic bytes
-(every source tile, K and V, read once): its duration is timed with HIP
-events on the launch stream with the 256 MB Infinity Cache flushed before
-each launch by reading a 512 MB buffer (a read leaves no dirty lines whose
-write-back would compete with the timed launch), so no byte of the timed
-launch is served from a cache.
+(every source tile, K and V, read once): its duration is timed with a pair
+of HIP events that the library attaches to the decode kernel's own start and
+end (kvs_time_next_launch, i.e. hipExtLaunchKernel; the partition merge and
+the launch latency are reported apart as avg_call_us), with the 256 MB
+Infinity Cache flushed before each launch by reading a 512 MB buffer (a read
+leaves no dirty lines whose write-back would compete with the timed launch),
+so no byte of the timed launch is served from a cache.
 ``cpu_baseline`` times the fp64 oracle on a bounded sample of sequences.
 """
 import argparse
@@ -426,13 +428,14 @@ def prefill_main(args, workload):
         for l in layers:
             append(l)
             if record:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0, e1, k0, k1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+                K.kvs_time_next_launch(k0, k1, stream)
                 e0.record(stream)
             K.kvs_attn_prefill_chunk(plan, cache, l, qs[l], seq_len, causal=True, out=outs[l],
                                      stream=stream)
             if record:
                 e1.record(stream)
-                ev[l].append((e0, e1))
+                ev[l].append((e0, e1, k0, k1))
 
     for _ in range(args.warmup):
         step()
@@ -444,8 +447,9 @@ def prefill_main(args, workload):
     t1.record(stream)
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / args.steps
-    us = sum(e0.elapsed_time(e1) for l in layers for (e0, e1) in ev[l]) * 1e3 / (
-        args.steps * len(layers))
+    n_calls = args.steps * len(layers)
+    us = sum(k0.elapsed_time(k1) for l in layers for (e0, e1, k0, k1) in ev[l]) * 1e3 / n_calls
+    call_us = sum(e0.elapsed_time(e1) for l in layers for (e0, e1, k0, k1) in ev[l]) * 1e3 / n_calls
     achieved = flops / (us * 1e-6) / 1e12
     res = {"metric": "shared-KV prefill chunk attn: prefill tokens/s and MFMA utilisation",
            "value": n * 1000.0 / ms, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -458,7 +462,9 @@ def prefill_main(args, workload):
            "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                         "traffic": None, "kernel": kernel,
-                        "flops_per_launch": flops, "avg_launch_us": us}}
+                        "flops_per_launch": flops, "avg_launch_us": us,
+                        "timing": "HIP events on the kernel's own start and end (hipExtLaunchKernel)",
+                        "avg_call_us": call_us}}
     if fact:
         res["config"] |= {"basis_rank": wl.basis_rank, "resid_rank_max": wl.resid_rank_max,
                           "rank16_frac": wl.rank16_frac}
@@ -732,16 +738,17 @@ def main():
         for _ in range(args.roofline_passes):
             for l in group:
                 flush.sum(dim=0)
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
+                e0, e1, k0, k1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+                K.kvs_time_next_launch(k0, k1, stream)
                 e0.record(stream)
                 decode(l)
                 e1.record(stream)
-                timed.setdefault(l, []).append((e0, e1))
+                timed.setdefault(l, []).append((e0, e1, k0, k1))
     torch.cuda.synchronize()
 
-    def avg_us(layers):
-        d = [e0.elapsed_time(e1) * 1e3 for l in layers for (e0, e1) in timed[l]]
+    def avg_us(layers, kernel_only=True):
+        d = [(k0.elapsed_time(k1) if kernel_only else e0.elapsed_time(e1)) * 1e3
+             for l in layers for (e0, e1, k0, k1) in timed[l]]
         return sum(d) / len(d)
 
     dom = single if single else mixed
@@ -755,13 +762,16 @@ def main():
                                   decode_kernel_name(wl, not single) + ", "
                                   + ("single-source layer" if single else "two-source layer")),
                        "bytes_per_launch": nbytes, "avg_launch_us": us,
+                       "timing": "HIP events on the kernel's own start and end (hipExtLaunchKernel)",
+                       "avg_call_us": avg_us(dom, kernel_only=False),
                        "launches": sum(len(timed[l]) for l in dom), "cache": "flushed"}
     if single and mixed:
         us2 = avg_us(mixed)
         b2 = call_bytes[mixed[0]]
         res["roofline_two_source"] = {"achieved": b2 / (us2 * 1e-6) / 1e9,
                                       "frac": b2 / (us2 * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                                      "bytes_per_launch": b2, "avg_launch_us": us2}
+                                      "bytes_per_launch": b2, "avg_launch_us": us2,
+                                      "avg_call_us": avg_us(mixed, kernel_only=False)}
     if fact:
         # router statistics: the same cache-flushed launches with the entropy
         # and peak side output, then the rank choice over every layer's

@@ -430,6 +430,20 @@ KVS_API kvs_status kvs_route_ranks(const kvs_plan* plan, const float* stats, int
                                    const int32_t* n_keys, int32_t batch,
                                    const kvs_router* router, uint8_t* rank_out, void* stream);
 
+/* Kernel timing, for benchmarks and profilers (no passage of the pages: it
+ * measures the calls above).  Arms the calling thread's next
+ * kvs_attn_decode, kvs_attn_decode_stats or kvs_attn_prefill_chunk call so
+ * that its main kernel (the split-K partition kernel, or the prefill kernel)
+ * is launched with hipExtLaunchKernel and records start_event when it starts
+ * executing and stop_event when it ends; hipEventElapsedTime of the pair is
+ * that kernel's duration.  A merge launch that follows is outside the pair.
+ *   start_event, stop_event  hipEvent_t handles the caller created (either
+ *                            may be NULL; both NULL disarms); the caller
+ *                            keeps ownership
+ * The next such call consumes the arming whether it succeeds or not.
+ * Always KVS_OK. */
+KVS_API kvs_status kvs_time_next_launch(void* start_event, void* stop_event);
+
 /* Description of the last error on this thread ("" if none). */
 KVS_API const char* kvs_last_error(void);
 

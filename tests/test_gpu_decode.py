@@ -179,3 +179,26 @@ def test_full_size_sampled(name, layers, sample_b):
             max_abs, rel = errors(got[b:b + 1], ref)
             note(f"   layer {l} b {b}: max_abs {max_abs:.2e} rel {rel:.2e}")
             assert max_abs <= 1e-2 and rel <= 5e-3
+
+
+def test_timed_launch_events_bracket_the_kernel():
+    """kvs_time_next_launch: the armed call's output is the unarmed call's, its
+    kernel events give a positive duration no longer than the whole call, and
+    the arming is consumed by one call (the next call leaves the events alone)."""
+    wl, B, ctx, lens = CASES["peaky_hd128"]
+    note("[timed launch] decode with kernel events, S = 4")
+    d = Dense(wl, B, ctx, lens)
+    ref = d.decode(0, n_splits=4)
+    e0, e1, k0, k1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+    K.kvs_time_next_launch(k0, k1)
+    e0.record()
+    got = d.decode(0, n_splits=4)
+    e1.record()
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    kernel_ms, call_ms = k0.elapsed_time(k1), e0.elapsed_time(e1)
+    assert 0.0 < kernel_ms <= call_ms
+    stamp = k1.elapsed_time(k0)
+    d.decode(0, n_splits=4)            # not armed: k0, k1 keep their timestamps
+    torch.cuda.synchronize()
+    assert k1.elapsed_time(k0) == stamp

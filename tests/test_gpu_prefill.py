@@ -90,3 +90,17 @@ def test_prefill_full_size_sampled():
             max_abs, rel = errors(got[:, i], ref)
             note(f"   layer {layer} row {i}: max_abs {max_abs:.2e} rel {rel:.2e}")
             assert max_abs <= 1e-2 and rel <= 5e-3
+
+
+def test_timed_launch_events_on_prefill():
+    """The prefill kernel launched with kernel events gives the same output and
+    a positive kernel duration."""
+    wl, B, ctx, lens, n, causal = CASES["g8_hd64"]
+    note("[timed launch] prefill with kernel events")
+    d = Dense(wl, B, ctx, lens)
+    q, ref = _prefill(d, 0, n)
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    K.kvs_time_next_launch(k0, k1)
+    _, got = _prefill(d, 0, n, q=q)
+    assert torch.equal(got, ref)
+    assert k0.elapsed_time(k1) > 0.0
