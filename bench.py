@@ -263,7 +263,7 @@ def record_profile(prof_dir, kernel, workload, s):
     top = [r for r in allk if "kvs::" in r["Name"]] + [r for r in allk if "kvs::" not in r["Name"]][:4]
     alg = algorithmic_bytes(wl, kernel)
     fetch, write = s["FETCH_SIZE"]["bytes_per_dispatch"], s["WRITE_SIZE"]["bytes_per_dispatch"]
-    cmd = (f"python3 bench.py --workload {workload} --steps 2 --warmup 1" if prefill
+    cmd = (f"python3 bench.py --workload {workload} --steps 8 --warmup 2" if prefill
            else f"python3 bench.py --workload {workload} --roofline-only")
     lines = [
         f"# `{kernel}` on `{workload}`", "",
@@ -781,14 +781,14 @@ def main():
         for _ in range(args.roofline_passes):
             for l in dom:
                 flush.sum(dim=0)
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
+                e0, e1, k0, k1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+                K.kvs_time_next_launch(k0, k1, stream)
                 e0.record(stream)
                 K.kvs_attn_decode_stats(plan, cache, l, qs[l], seq_len, wl.ctx, out=outs[l],
                                         stats=stats[l], n_splits=n_splits, workspace=ws,
                                         stream=stream)
                 e1.record(stream)
-                ev_s.append((e0, e1))
+                ev_s.append((e0, e1, k0, k1))
         router = K.kvs_router(0.5, 0.8, 0.5, wl.resid_rank_max, wl.resid_rank_max // 2, 0)
         ranks = torch.empty(B, dtype=torch.uint8, device="cuda")
         K.kvs_route_ranks(plan, stats, seq_len, router, rank_out=ranks, stream=stream)
@@ -798,9 +798,13 @@ def main():
             K.kvs_route_ranks(plan, stats, seq_len, router, rank_out=ranks, stream=stream)
         r1.record(stream)
         torch.cuda.synchronize()
-        us_s = sum(e0.elapsed_time(e1) for e0, e1 in ev_s) * 1e3 / len(ev_s)
+        us_s = sum(k0.elapsed_time(k1) for e0, e1, k0, k1 in ev_s) * 1e3 / len(ev_s)
+        call_s = sum(e0.elapsed_time(e1) for e0, e1, k0, k1 in ev_s) * 1e3 / len(ev_s)
+        call = res["roofline"]["avg_call_us"]
         res["router"] = {"decode_with_stats_us": us_s, "decode_us": us,
                          "stats_overhead_frac": us_s / us - 1.0,
+                         "call_with_stats_us": call_s, "call_us": call,
+                         "stats_overhead_call_frac": call_s / call - 1.0,
                          "route_us": r0.elapsed_time(r1) * 1e3 / 10,
                          "route_sets": L, "routed_ranks": ranks.cpu().tolist()}
     del flush
