@@ -16,10 +16,12 @@
 // Decomposition (gfx950, v_mfma_f32_32x32x16_bf16; lane l of A/B holds row or
 // column l%32 and k = 8*(l/32)+e; result register r of lane l is row
 // 8*(r/4) + 4*(l/32) + r%4, column l%32):
-//   workgroup = 4 waves sharing one KV head: HW = min(G, 4) query heads x
-//   4/HW blocks of 32 consecutive query positions; each wave owns 32 query
-//   rows of one head.  Per 64-key tile (one cache page):
-//     staging  all 256 threads copy the K page into LDS as [64 keys][hd]
+//   workgroup = NW waves sharing one KV head (NW = 8 for hd 128: one
+//   workgroup per CU, two waves per SIMD, every staged tile serving 256 query
+//   rows; NW = 4 for hd 64, two workgroups per CU): HW = min(G, 4) query
+//   heads x NW/HW blocks of 32 consecutive query positions; each wave owns
+//   32 query rows of one head.  Per 64-key tile (one cache page):
+//     staging  all threads copy the K page into LDS as [64 keys][hd]
 //              (16-byte chunks XOR-swizzled by key) and the V page as V^T
 //              [hd][64+4 keys]; keys past the sequence end are zeroed (cache
 //              memory there is unwritten).  Registers hold the next tile's
@@ -117,14 +119,22 @@ __device__ __forceinline__ uint4 mix_chunk(const uint4& a, const uint4& b, float
   return r;
 }
 
+// Waves per workgroup.  Eight waves sharing each staged tile halve the
+// staging loads and LDS writes per MFMA against two 4-wave workgroups per CU
+// (hd 128: 395 vs 427 us per DepthGraft chunk layer); the hd-64 V staging
+// needs at least two key pairs per thread, i.e. at most four waves.
+template <int HD> struct Waves { static constexpr int NW = HD == 128 ? 8 : 4; };
+
 template <int HD, int G, int NSRC>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
+__global__ __launch_bounds__(64 * Waves<HD>::NW, 8 / Waves<HD>::NW) void prefill_kernel(PrefillParams a) {
+  constexpr int NW = Waves<HD>::NW;
+  constexpr int NT = 64 * NW;
   constexpr int HW = G < 4 ? G : 4;          // heads per workgroup
-  constexpr int PB = 4 / HW;                 // 32-row position blocks per workgroup
+  constexpr int PB = NW / HW;                // 32-row position blocks per workgroup
   constexpr int NCH = HD / 8;                // 16-byte chunks per key row
   constexpr int KS = HD / 16;                // MFMA k-steps over the head dim
   constexpr int MB = HD / 32;                // 32-dim blocks of O^T
-  constexpr int KCH = 64 * NCH / 256;        // K chunks staged per thread per source
+  constexpr int KCH = 64 * NCH / NT;         // K chunks staged per thread per source
   constexpr int VCH = KCH;                   // V chunks staged per thread per source
   static_assert(VCH == 2 || VCH == 4, "V staging stores 2 or 4 dwords per dim row");
 
@@ -190,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
       const uint16_t* kp = a.k_pool + (s == 0 ? so0 : so1) + tile;
       const uint16_t* vp = a.v_pool + (s == 0 ? so0 : so1) + tile;
 #pragma unroll
-      for (int u = 0; u < KCH; ++u) kst[s][u] = *reinterpret_cast<const uint4*>(kp + (tid + 256 * u) * 8);
+      for (int u = 0; u < KCH; ++u) kst[s][u] = *reinterpret_cast<const uint4*>(kp + (tid + NT * u) * 8);
 #pragma unroll
       for (int u = 0; u < VCH; ++u) vst[s][u] = *reinterpret_cast<const uint4*>(vp + v_chunk(u) * 8);
     }
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
       // cache layout chunk index -> (key, chunk)
-      const int qi = tid + 256 * u;
+      const int qi = tid + NT * u;
       constexpr int NCW = NCH / kWays, KPP = 64 / kWays;   // chunks per lane, keys per pass
       const int j = qi / (NCW * 64), cc = (qi / 64) % NCW, kk = (qi % 64) / kWays, w = qi % kWays;
       const int key = KPP * j + kk, c = kWays * cc + w;
@@ -382,11 +392,11 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams a) {
 template <int HD, int G, int NSRC>
 int run_prefill(PrefillParams p, int B, hipStream_t st, const KernelEvents& ev) {
   constexpr int HW = G < 4 ? G : 4;
-  constexpr int PB = 4 / HW;
+  constexpr int PB = Waves<HD>::NW / HW;
   p.head_groups = G / HW;
   p.n_pos_groups = (p.n + PB * kRows - 1) / (PB * kRows);
   dim3 grid(p.n_pos_groups * p.head_groups * p.n_kv_heads, B);
-  launch_main(ev, prefill_kernel<HD, G, NSRC>, grid, dim3(256), st, p);
+  launch_main(ev, prefill_kernel<HD, G, NSRC>, grid, dim3(64 * Waves<HD>::NW), st, p);
   return (int)hipGetLastError();
 }
 
