@@ -24,9 +24,9 @@
 //     staging  all threads copy the K page into LDS as [64 keys][hd]
 //              (16-byte chunks XOR-swizzled by key) and the V page as V^T
 //              [hd][64+4 keys]; keys past the sequence end are zeroed (cache
-//              memory there is unwritten).  Registers hold the next tile's
-//              global loads while the current tile is computed; one barrier
-//              per tile (double-buffered LDS).
+//              memory there is unwritten).  Two register stages hold the
+//              global loads of the next two tiles while the current tile is
+//              computed; one barrier per tile (double-buffered LDS).
 //     S^T = K Q^T   16 MFMAs (2 blocks of 32 keys x hd/16 steps): each lane
 //              ends up with 32 scores of one query row (its column).
 //     softmax  online, per query row, in registers; the two lanes of a row
@@ -188,11 +188,16 @@ __global__ __launch_bounds__(64 * Waves<HD>::NW, 8 / Waves<HD>::NW) void prefill
   const int64_t so0 = (int64_t)a.slot0 * a.slot_stride;
   const int64_t so1 = (int64_t)a.slot1 * a.slot_stride;
 
-  uint4 kst[NSRC][KCH], vst[NSRC][VCH];
+  struct Stage {
+    uint4 k[NSRC][KCH], v[NSRC][VCH];
+    int entry;                               // page-table entry of the staged tile
+  };
+  Stage sa, sb;                              // register stages of alternate tiles
   // V chunk u of this thread: key pair (tid / (HD/4)) * VCH + u, dims
   // 4 * (tid % (HD/4)) .. +3 (16-byte unit pair * HD/4 + dim group)
   auto v_chunk = [&](int u) { return ((tid / (HD / 4)) * VCH + u) * (HD / 4) + tid % (HD / 4); };
-  auto load_tile = [&](int entry) {
+  auto load_tile = [&](int entry, Stage& st) {
+    st.entry = entry;
     const int page = (unsigned)entry < (unsigned)a.n_phys_pages ? entry : 0;   // corrupt entry: read page 0, masked below
     const int64_t tile = ((int64_t)page * a.n_kv_heads + kvh) * (64 * HD);
 #pragma unroll
@@ -200,12 +205,12 @@ __global__ __launch_bounds__(64 * Waves<HD>::NW, 8 / Waves<HD>::NW) void prefill
       const uint16_t* kp = a.k_pool + (s == 0 ? so0 : so1) + tile;
       const uint16_t* vp = a.v_pool + (s == 0 ? so0 : so1) + tile;
 #pragma unroll
-      for (int u = 0; u < KCH; ++u) kst[s][u] = *reinterpret_cast<const uint4*>(kp + (tid + NT * u) * 8);
+      for (int u = 0; u < KCH; ++u) st.k[s][u] = *reinterpret_cast<const uint4*>(kp + (tid + NT * u) * 8);
 #pragma unroll
-      for (int u = 0; u < VCH; ++u) vst[s][u] = *reinterpret_cast<const uint4*>(vp + v_chunk(u) * 8);
+      for (int u = 0; u < VCH; ++u) st.v[s][u] = *reinterpret_cast<const uint4*>(vp + v_chunk(u) * 8);
     }
   };
-  auto store_tile = [&](int t, int entry, int buf) {
+  auto store_tile = [&](int t, int entry, int buf, const Stage& st) {
     const int key0 = t * 64;
     const bool page_ok = (unsigned)entry < (unsigned)a.n_phys_pages;
 #pragma unroll
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(64 * Waves<HD>::NW, 8 / Waves<HD>::NW) void prefill
       constexpr int NCW = NCH / kWays, KPP = 64 / kWays;   // chunks per lane, keys per pass
       const int j = qi / (NCW * 64), cc = (qi / 64) % NCW, kk = (qi % 64) / kWays, w = qi % kWays;
       const int key = KPP * j + kk, c = kWays * cc + w;
-      uint4 v = NSRC == 2 ? mix_chunk(kst[0][u], kst[NSRC - 1][u], a.w0, a.w1) : kst[0][u];
+      uint4 v = NSRC == 2 ? mix_chunk(st.k[0][u], st.k[NSRC - 1][u], a.w0, a.w1) : st.k[0][u];
       *reinterpret_cast<uint4*>(&k_lds[buf][key * HD + ((c ^ (key & (NCH - 1))) * 8)]) = v;
     }
     // V^T: this thread holds VCH consecutive key pairs of its 4 dims (a
@@ -226,7 +231,7 @@ __global__ __launch_bounds__(64 * Waves<HD>::NW, 8 / Waves<HD>::NW) void prefill
       uint32_t w[4][VCH];
 #pragma unroll
       for (int u = 0; u < VCH; ++u) {
-        const uint4 v = NSRC == 2 ? mix_chunk(vst[0][u], vst[NSRC - 1][u], a.w0, a.w1) : vst[0][u];
+        const uint4 v = NSRC == 2 ? mix_chunk(st.v[0][u], st.v[NSRC - 1][u], a.w0, a.w1) : st.v[0][u];
         w[0][u] = v.x;
         w[1][u] = v.y;
         w[2][u] = v.z;
@@ -263,20 +268,19 @@ __global__ __launch_bounds__(64 * Waves<HD>::NW, 8 / Waves<HD>::NW) void prefill
   float m_run = -INFINITY, l_run = 0.f;
   const float bump_gap = kBumpLog2 / a.scale_log2;   // in raw score units
 
-  // page-table entries of tiles t and t + 1, read a tile ahead of their use
-  // so that no scalar load sits between the tile's staging steps
-  int pt_cur = n_tiles > 0 ? pt[0] : 0;
-  int pt_next = n_tiles > 1 ? pt[1] : 0;
-  if (n_tiles > 0) load_tile(pt_cur);
-  for (int t = 0; t < n_tiles; ++t) {
+  // Register stages: tile t's loads were issued two tiles before its LDS
+  // stores (two stages, the loop unrolled by two so each is static).
+  // Page-table entries are read a tile before the loads that use them.
+  int pt_a = n_tiles > 2 ? pt[2] : 0;
+  if (n_tiles > 0) load_tile(pt[0], sa);
+  if (n_tiles > 1) load_tile(pt[1], sb);
+  auto tile_step = [&](int t, Stage& st) {
     const int buf = t & 1;
-    const int pt_after = pt[min(t + 2, n_tiles - 1)];
-    store_tile(t, pt_cur, buf);
-    if (t + 1 < n_tiles) load_tile(pt_next);
-    pt_cur = pt_next;
-    pt_next = pt_after;
+    const int pt_b = pt[min(t + 3, n_tiles - 1)];
+    store_tile(t, st.entry, buf, st);
+    if (t + 2 < n_tiles) load_tile(pt_a, st);
+    pt_a = pt_b;
     __syncthreads();
-
     // ---- S^T = K Q^T: two 32-key blocks
     f32x16_t s[2];
 #pragma unroll
@@ -365,6 +369,10 @@ __global__ __launch_bounds__(64 * Waves<HD>::NW, 8 / Waves<HD>::NW) void prefill
         const uint16_t* vrow = &v_lds[buf][vrow_of(d) * kVRow + 16 * sp + 8 * hh];
         o[mb] = mfma32(*reinterpret_cast<const uint4*>(vrow), pb[sp], o[mb]);
       }
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile_step(t, sa);
+    if (t + 1 < n_tiles) tile_step(t + 1, sb);
   }
 
   // ---- normalise and store this lane's row: dims 32mb + 8(r/4) + 4hh + r%4
