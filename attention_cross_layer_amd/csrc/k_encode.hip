@@ -15,7 +15,8 @@
 //   U_l  = Rmax leading right singular vectors of the layer's residual rows
 // (rows sign-normalised: largest-magnitude entry positive).
 //
-// Encoder (one wave per 32 tokens of one KV head and one of K / V;
+// Encoder (one wave per 32 tokens of one KV head and one of K / V, four
+// waves per workgroup sharing the basis staged in LDS;
 // v_mfma_f32_32x32x16_bf16, lane l of A/B holding row or column l%32 and
 // k = 8(l/32)+e, result register r of lane l = row 8(r/4)+4(l/32)+r%4,
 // column l%32):
@@ -99,18 +100,21 @@ struct EncodeParams {
   int32_t residual_mode;
 };
 
-// grid (ceil(n/32), 2 Hkv, B), one wave
+constexpr int kEncWaves = 4;      // waves per workgroup, 32 tokens each, sharing the staged B^T
+
+// grid (ceil(n / (32 kEncWaves)), 2 Hkv, B), kEncWaves waves
 template <int HD>
-__global__ __launch_bounds__(64) void encode_kernel(EncodeParams a) {
+__global__ __launch_bounds__(64 * kEncWaves) void encode_kernel(EncodeParams a) {
   constexpr int KS = HD / 16;
   constexpr int MB = HD / 32;
   __shared__ __attribute__((aligned(16))) uint16_t bt[HD * kBT];
 
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, col = lane & 31;
   const int kvh = blockIdx.y >> 1, kv = blockIdx.y & 1, b = blockIdx.z;
   const EncodeSide& s = a.side[kv];
-  const int i = blockIdx.x * 32 + col;
+  const int i = (blockIdx.x * kEncWaves + wave) * 32 + col;
   const bool ok = i < a.n;
   const size_t row = ((size_t)b * a.n + (ok ? i : a.n - 1)) * a.n_kv_heads + kvh;
   const uint16_t* xr = s.x + row * HD;
@@ -118,7 +122,7 @@ __global__ __launch_bounds__(64) void encode_kernel(EncodeParams a) {
   const uint16_t* bh = s.basis + (size_t)kvh * kR * HD;
 
   // B^T into LDS: position swz16(i) of row d holds B[i][d]
-  for (int idx = lane; idx < kR * HD / 8; idx += 64) {
+  for (int idx = tid; idx < kR * HD / 8; idx += 64 * kEncWaves) {
     const int ci = idx / (HD / 8), d0 = (idx % (HD / 8)) * 8;
     const uint4 v = *reinterpret_cast<const uint4*>(bh + ci * HD + d0);
     uint16_t* dst = bt + d0 * kBT + swz16(ci);
@@ -473,8 +477,8 @@ __global__ __launch_bounds__(1024) void eig_kernel(EigParams a) {
 
 template <int HD>
 int run_encode(const EncodeParams& p, int batch, hipStream_t st) {
-  dim3 grid((p.n + 31) / 32, 2 * p.n_kv_heads, batch);
-  hipLaunchKernelGGL(encode_kernel<HD>, grid, dim3(64), 0, st, p);
+  dim3 grid((p.n + 32 * kEncWaves - 1) / (32 * kEncWaves), 2 * p.n_kv_heads, batch);
+  hipLaunchKernelGGL(encode_kernel<HD>, grid, dim3(64 * kEncWaves), 0, st, p);
   return (int)hipGetLastError();
 }
 

@@ -685,33 +685,37 @@ FactFn pick(int hd, int G) {
 
 // ---------------------------------------------------------------- writes
 
-// One thread per (sequence, token, KV head).  A token's granule offset is the
-// sum of ceil(r/8) over the page's earlier tokens: ranks of tokens this call
-// writes come from `rank`, earlier ones from the page's meta entries.
-__global__ __launch_bounds__(256) void fact_append_kernel(FactAppendLaunch a) {
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = (long long)a.batch * a.n * a.n_kv_heads;
-  if (idx >= total) return;
-  const int kvh = (int)(idx % a.n_kv_heads);
-  const long long bi = idx / a.n_kv_heads;
-  const int i = (int)(bi % a.n);
-  const int b = (int)(bi / a.n);
+// One wave per (page the append touches, KV head, sequence); lane t is
+// token slot t of the page.  A token's granule offset is the exclusive
+// prefix sum of ceil(r/8) over the page's earlier slots, taken across the
+// wave: ranks of tokens this call writes come from `rank`, earlier ones from
+// the page's meta entries.
+__global__ __launch_bounds__(64) void fact_append_kernel(FactAppendLaunch a) {
+  const int t = threadIdx.x;
+  const int kvh = blockIdx.y, b = blockIdx.z;
   const int sp = a.start_pos[b];
-  const int pos = sp + i;
-  if (pos < 0 || pos >= a.max_ctx) return;
-  const int page = a.page_table[(size_t)b * a.pages_per_seq + pos / kPage];
-  if (page < 0 || page >= a.n_phys_pages) return;
-  const int t = pos % kPage;
-  const size_t page_kv = (size_t)page * a.n_kv_heads + kvh;
-  const size_t src_row = ((size_t)b * a.n + i) * a.n_kv_heads + kvh;
+  const int end = min(sp + a.n, a.max_ctx);            // positions [max(sp, 0), end) are written
+  const int lp = max(sp, 0) / kPage + (int)blockIdx.x;  // logical page of this wave
+  if (lp * kPage >= end) return;                        // uniform
+  const int page = a.page_table[(size_t)b * a.pages_per_seq + lp];
+  if (page < 0 || page >= a.n_phys_pages) return;       // uniform
+  const int pos = lp * kPage + t;
+  const bool fresh = pos >= sp && pos < end;
+  const int i = pos - sp;
   const uint8_t* rk = a.rank + (size_t)b * a.n;
   uint16_t* meta = static_cast<uint16_t*>(a.rank_pool) + (size_t)page * kPage;
-  const int r = min((int)rk[i], kRM);
-  int g0 = 0;
-  for (int u = 0, pu = pos - t; u < t; ++u, ++pu) {
-    const int ru = pu >= sp ? (int)rk[pu - sp] : (int)(meta[u] & 0xffu);
-    g0 += (min(ru, kRM) + 7) >> 3;
+  const int r = fresh ? min((int)rk[i], kRM) : (pos < sp ? min((int)(meta[t] & 0xffu), kRM) : 0);
+  const int ng = (r + 7) >> 3;
+  int incl = ng;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (t >= off) incl += v;
   }
+  const int g0 = incl - ng;
+  if (!fresh) return;
+  const size_t page_kv = (size_t)page * a.n_kv_heads + kvh;
+  const size_t src_row = ((size_t)b * a.n + i) * a.n_kv_heads + kvh;
   if (a.coef_slot >= 0) {
     const size_t base = ((size_t)a.coef_slot * a.n_phys_pages * a.n_kv_heads + page_kv) * kPage * kR;
     const uint16_t* ck = static_cast<const uint16_t*>(a.ck) + src_row * kR;
@@ -729,7 +733,6 @@ __global__ __launch_bounds__(256) void fact_append_kernel(FactAppendLaunch a) {
   }
   {
     const size_t lbase = (size_t)a.layer * a.n_phys_pages * a.n_kv_heads + page_kv;
-    const int ng = (r + 7) >> 3;
     // codes j >= r are stored as zero
     uint32_t keep[4];
 #pragma unroll
@@ -806,9 +809,11 @@ int launch_fact_decode(const FactDecodeLaunch& a, void* stream) {
 }
 
 int launch_fact_append(const FactAppendLaunch& a, void* stream) {
-  const long long total = (long long)a.batch * a.n * a.n_kv_heads;
-  if (total == 0) return 0;
-  hipLaunchKernelGGL(fact_append_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+  if (a.batch == 0 || a.n == 0) return 0;
+  // pages a chunk of n positions can touch: one more than it fills when it
+  // starts mid-page
+  const unsigned pages = (unsigned)((a.n + kPage - 1) / kPage + 1);
+  hipLaunchKernelGGL(fact_append_kernel, dim3(pages, a.n_kv_heads, a.batch), dim3(64), 0,
                      static_cast<hipStream_t>(stream), a);
   return (int)hipGetLastError();
 }
