@@ -142,3 +142,60 @@ def test_factorized_append_layout_bit_exact():
                     assert int(dkp[0, page, h, goff * 8 + j]) == want_k, (b, pos, h, j)
                     assert int(dvp[0, page, h, goff * 8 + j]) == want_v, (b, pos, h, j)
             goff += (r + 7) // 8
+
+
+def test_factorized_append_skips_positions_out_of_range():
+    """Positions below 0 or at max_ctx and beyond are skipped: sequence 0's
+    chunk starts before position 0, sequence 1's runs past the context end.
+    The written tokens' meta entries (rank | granule offset << 8), codes and
+    scales follow the layout; the skipped slots stay untouched (zero)."""
+    wl = F.with_(n_layers=2, n_q_heads=4, n_kv_heads=2, head_dim=64)
+    B, ctx, n = 2, 192, 70
+    import attention_cross_layer_amd as K
+    note(f"[factorized append range] B={B} ctx={ctx} n={n} start=(-10, {ctx - 30})")
+    src, w = datagen.share_map(wl)
+    cfg = K.make_config(wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, "bf16", B, ctx,
+                        kind=K.KVS_FACTORIZED, basis_rank=32, resid_rank_max=16)
+    plan = K.kvs_share_plan(cfg, src, w)
+    c = K.Cache(plan, "cuda")
+    for t in (c.ck_pool, c.cv_pool, c.dk_pool, c.dv_pool, c.sk_pool, c.rank_pool):
+        t.zero_()
+    g = torch.Generator().manual_seed(11)
+    rank = torch.randint(0, 17, (B, n), generator=g).to(torch.uint8)
+    ck = torch.randn(B, n, 2, 32, generator=g).to(torch.bfloat16)
+    cv = torch.randn(B, n, 2, 32, generator=g).to(torch.bfloat16)
+    dk = torch.randint(-127, 128, (B, n, 2, 16), generator=g).to(torch.int8)
+    dv = torch.randint(-127, 128, (B, n, 2, 16), generator=g).to(torch.int8)
+    sk = (torch.rand(B, n, 2, generator=g) + 0.5).to(torch.float16)
+    sv = (torch.rand(B, n, 2, generator=g) + 0.5).to(torch.float16)
+    starts = [-10, ctx - 30]
+    sp = torch.tensor(starts, dtype=torch.int32).cuda()
+    K.kvs_append_factorized(plan, c, 0, ck.cuda(), cv.cuda(), dk.cuda(), dv.cuda(), sk.cuda(),
+                            sv.cuda(), rank.cuda(), sp)
+    torch.cuda.synchronize()
+    P = c.sizes.n_phys_pages
+    pt = c.page_table.cpu().view(B, -1)
+    dkp = c.dk_pool.cpu().view(torch.int8).view(-1, P, 2, 128 * 8)
+    skp = c.sk_pool.cpu().view(torch.int16).view(-1, P, 2, 64)
+    meta = c.rank_pool.cpu().view(torch.int16).view(P, 64).to(torch.int32) & 0xffff
+    sk16 = sk.view(torch.int16)
+    for b in range(B):
+        written = {starts[b] + i: i for i in range(n) if 0 <= starts[b] + i < ctx}
+        goff = 0
+        for pos in range(ctx):
+            page, t = int(pt[b, pos // 64]), pos % 64
+            if t == 0:
+                goff = 0
+            if pos not in written:
+                assert int(meta[page, t]) == 0, (b, pos)
+                assert all(int(skp[0, page, h, t]) == 0 for h in range(2)), (b, pos)
+                continue
+            i = written[pos]
+            r = int(rank[b, i])
+            assert int(meta[page, t]) == r | (goff << 8), (b, pos)
+            for h in range(2):
+                assert int(skp[0, page, h, t]) == int(sk16[b, i, h]), (b, pos, h)
+                for j in range(8 * ((r + 7) // 8)):
+                    want = int(dk[b, i, h, j]) if j < r else 0
+                    assert int(dkp[0, page, h, goff * 8 + j]) == want, (b, pos, h, j)
+            goff += (r + 7) // 8
