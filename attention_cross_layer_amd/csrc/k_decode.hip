@@ -503,13 +503,22 @@ struct MfmaPage {
   uint4 v[2][4];      // [ps][db]: 4 dwords (pairs) of dim 16db + l%16
 };
 
+// Waves per workgroup (one workgroup per (partition, KV head, sequence)).
+// Each wave loads one page and computes it before loading the next: with
+// 256 workgroups of 4 waves that keeps 16 MB in flight, and the streaming
+// rate is higher than with a second page in flight per wave (26.7 vs
+// 28.4 us per tinyllama_cla2 layer) or with 8 or 2 waves (27.4, 30.4 us):
+// more requests in flight lower the HBM efficiency, fewer leave it idle.
+constexpr int kMfmaWaves = 4;
+
 template <int G>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams a) {
+__global__ __launch_bounds__(64 * kMfmaWaves) void decode_mfma_kernel(DecodeParams a) {
+  constexpr int NW = kMfmaWaves;
   constexpr int HD = 64;
   static_assert(G <= 16, "one 16-column block of heads");
-  __shared__ float mrg_o[4][G][HD];
-  __shared__ float mrg_m[4][G];
-  __shared__ float mrg_l[4][G];
+  __shared__ float mrg_o[NW][G][HD];
+  __shared__ float mrg_m[NW][G];
+  __shared__ float mrg_l[NW][G];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -540,7 +549,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams a) {
 
   auto next_page = [&](int from) {
     int p = from;
-    while (p < pe && (unsigned)pt[p] >= (unsigned)a.n_phys_pages) p += 4;
+    while (p < pe && (unsigned)pt[p] >= (unsigned)a.n_phys_pages) p += NW;
     return p;
   };
   auto load = [&](int pg, MfmaPage& r) {
@@ -642,19 +651,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams a) {
       for (int db = 0; db < 4; ++db) o[db] = mfma16(pf[ps], r.v[ps][db], o[db]);
   };
 
-  // two page buffers: the next page's loads are in flight during a compute
-  MfmaPage bufA, bufB;
-  int pg = next_page(pb + wave);
-  if (pg < pe) load(pg, bufA);
-  while (pg < pe) {
-    const int pn = next_page(pg + 4);
-    if (pn < pe) load(pn, bufB);
+  MfmaPage bufA;
+  for (int pg = next_page(pb + wave); pg < pe; pg = next_page(pg + NW)) {
+    load(pg, bufA);
     compute(pg, bufA);
-    if (pn >= pe) break;
-    const int pn2 = next_page(pn + 4);
-    if (pn2 < pe) load(pn2, bufA);
-    compute(pn, bufB);
-    pg = pn2;
   }
 
   // ---- this wave's (O, m, l) to LDS; m in log2 units as the merge expects
@@ -677,15 +677,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams a) {
   __syncthreads();
 
   const size_t hq0 = (size_t)b * a.n_q_heads + (size_t)kvh * G;
-  for (int e = tid; e < G * HD; e += 256) {
+  for (int e = tid; e < G * HD; e += 64 * NW) {
     const int h = e / HD, d = e % HD;
     float M = mrg_m[0][h];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, mrg_m[w][h]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, mrg_m[w][h]);
     float ov = 0.f, l = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float f = dev::fast_exp2(mrg_m[w][h] - M);
         ov = fmaf(f, mrg_o[w][h][d], ov);
         l = fmaf(f, mrg_l[w][h], l);
@@ -707,7 +707,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams a) {
 template <int G>
 int run_decode_mfma(const DecodeParams& p, int B, hipStream_t st, const KernelEvents& ev) {
   dim3 grid(p.n_splits, p.n_kv_heads, B);
-  launch_main(ev, decode_mfma_kernel<G>, grid, dim3(256), st, p);
+  launch_main(ev, decode_mfma_kernel<G>, grid, dim3(64 * kMfmaWaves), st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return (int)e;
   hipLaunchKernelGGL((decode_merge_kernel<G, 64>), dim3(p.n_kv_heads, B), dim3(256), 0, st, p);
