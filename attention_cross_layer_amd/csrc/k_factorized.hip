@@ -238,7 +238,6 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
   int pb, pe;
   split_range(n_pages, split, S, pb, pe);
   const int32_t* pt = a.page_table + (size_t)b * a.pages_per_seq;
-  const size_t coef_page = (size_t)kPage * kR;          // elements per (page, head) of cK / cV
   const uint16_t* ck_base = a.ck + a.coef_off;
   const uint16_t* cv_base = a.cv + a.coef_off;
   const int8_t* dk_base = a.dk + a.resid_off;

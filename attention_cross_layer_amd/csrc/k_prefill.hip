@@ -16,11 +16,10 @@
 // Decomposition (gfx950, v_mfma_f32_32x32x16_bf16; lane l of A/B holds row or
 // column l%32 and k = 8*(l/32)+e; result register r of lane l is row
 // 8*(r/4) + 4*(l/32) + r%4, column l%32):
-//   workgroup = NW waves sharing one KV head (NW = 8 for hd 128: one
-//   workgroup per CU, two waves per SIMD, every staged tile serving 256 query
-//   rows; NW = 4 for hd 64, two workgroups per CU): HW = min(G, 4) query
-//   heads x NW/HW blocks of 32 consecutive query positions; each wave owns
-//   32 query rows of one head.  Per 64-key tile (one cache page):
+//   workgroup = NW = 8 waves sharing one KV head (one workgroup per CU, two
+//   waves per SIMD, every staged tile serving 256 query rows): HW = min(G, 4)
+//   query heads x NW/HW blocks of 32 consecutive query positions; each wave
+//   owns 32 query rows of one head.  Per 64-key tile (one cache page):
 //     staging  all threads copy the K page into LDS as [64 keys][hd]
 //              (16-byte chunks XOR-swizzled by key) and the V page as V^T
 //              [hd][64+4 keys]; keys past the sequence end are zeroed (cache
@@ -121,9 +120,9 @@ __device__ __forceinline__ uint4 mix_chunk(const uint4& a, const uint4& b, float
 
 // Waves per workgroup.  Eight waves sharing each staged tile halve the
 // staging loads and LDS writes per MFMA against two 4-wave workgroups per CU
-// (hd 128: 395 vs 427 us per DepthGraft chunk layer); the hd-64 V staging
-// needs at least two key pairs per thread, i.e. at most four waves.
-template <int HD> struct Waves { static constexpr int NW = HD == 128 ? 8 : 4; };
+// (hd 128: 395 vs 427 us per DepthGraft chunk layer; hd 64: 144 vs 159 us
+// for a 2048-query chunk of the 1.1B shape).
+template <int HD> struct Waves { static constexpr int NW = 8; };
 
 template <int HD, int G, int NSRC>
 __global__ __launch_bounds__(64 * Waves<HD>::NW, 8 / Waves<HD>::NW) void prefill_kernel(PrefillParams a) {
@@ -136,7 +135,7 @@ __global__ __launch_bounds__(64 * Waves<HD>::NW, 8 / Waves<HD>::NW) void prefill
   constexpr int MB = HD / 32;                // 32-dim blocks of O^T
   constexpr int KCH = 64 * NCH / NT;         // K chunks staged per thread per source
   constexpr int VCH = KCH;                   // V chunks staged per thread per source
-  static_assert(VCH == 2 || VCH == 4, "V staging stores 2 or 4 dwords per dim row");
+  static_assert(VCH >= 1 && VCH <= 4, "V staging stores 1 to 4 dwords per dim row");
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][64 * HD];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][HD * kVRow];
@@ -254,10 +253,7 @@ __global__ __launch_bounds__(64 * Waves<HD>::NW, 8 / Waves<HD>::NW) void prefill
         uint32_t* row = reinterpret_cast<uint32_t*>(dst + vrow_of(4 * L + i) * kVRow);
         const int k0 = 2 * VCH * q;                          // first of this thread's keys
 #pragma unroll
-        for (int u = 0; u < VCH; u += 2) {
-          row[swz16(k0 + 2 * u) / 2] = w[i][u];
-          row[swz16(k0 + 2 * u) / 2 + 1] = w[i][u + 1];
-        }
+        for (int u = 0; u < VCH; ++u) row[swz16(k0 + 2 * u) / 2] = w[i][u];
       }
     }
   };
