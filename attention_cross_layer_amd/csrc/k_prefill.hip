@@ -122,11 +122,11 @@ __device__ __forceinline__ uint4 mix_chunk(const uint4& a, const uint4& b, float
 // staging loads and LDS writes per MFMA against two 4-wave workgroups per CU
 // (hd 128: 395 vs 427 us per DepthGraft chunk layer; hd 64: 144 vs 159 us
 // for a 2048-query chunk of the 1.1B shape).
-template <int HD> struct Waves { static constexpr int NW = 8; };
+constexpr int kWaves = 8;
 
 template <int HD, int G, int NSRC>
-__global__ __launch_bounds__(64 * Waves<HD>::NW, 8 / Waves<HD>::NW) void prefill_kernel(PrefillParams a) {
-  constexpr int NW = Waves<HD>::NW;
+__global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a) {
+  constexpr int NW = kWaves;
   constexpr int NT = 64 * NW;
   constexpr int HW = G < 4 ? G : 4;          // heads per workgroup
   constexpr int PB = NW / HW;                // 32-row position blocks per workgroup
@@ -396,11 +396,11 @@ __global__ __launch_bounds__(64 * Waves<HD>::NW, 8 / Waves<HD>::NW) void prefill
 template <int HD, int G, int NSRC>
 int run_prefill(PrefillParams p, int B, hipStream_t st, const KernelEvents& ev) {
   constexpr int HW = G < 4 ? G : 4;
-  constexpr int PB = Waves<HD>::NW / HW;
+  constexpr int PB = kWaves / HW;
   p.head_groups = G / HW;
   p.n_pos_groups = (p.n + PB * kRows - 1) / (PB * kRows);
   dim3 grid(p.n_pos_groups * p.head_groups * p.n_kv_heads, B);
-  launch_main(ev, prefill_kernel<HD, G, NSRC>, grid, dim3(64 * Waves<HD>::NW), st, p);
+  launch_main(ev, prefill_kernel<HD, G, NSRC>, grid, dim3(64 * kWaves), st, p);
   return (int)hipGetLastError();
 }
 
