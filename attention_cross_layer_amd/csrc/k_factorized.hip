@@ -295,7 +295,26 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
     r.dv[1] = ld8(r_dv, o1);
   };
 
-  // ---- the first page's requests go out before the query contraction
+  // ---- absorbed query: qt[h][i] = (row i of B^K, or U^K for i >= R) . q_h.
+  // The operands of a thread's first element are requested before the first
+  // page, so that waiting for them does not wait for the page as well.
+  constexpr int NE = NB * 4 * kW;
+  const int e0h = tid / kW, e0i = tid % kW;
+  const bool live0 = tid < NE && e0h < G;
+  uint4 x0[HD / 8], y0[HD / 8];
+  {
+    // threads without an element read row e0i of head 0's operands, unused
+    const uint16_t* row = e0i < kR ? a.bk + ((size_t)kvh * kR + e0i) * HD
+                                   : a.uk + ((size_t)kvh * kRM + (e0i - kR)) * HD;
+    const uint16_t* qr = a.q + ((size_t)b * a.n_q_heads + (size_t)kvh * G + (live0 ? e0h : 0)) * HD;
+#pragma unroll
+    for (int c = 0; c < HD / 8; ++c) {
+      x0[c] = *reinterpret_cast<const uint4*>(row + c * 8);
+      y0[c] = *reinterpret_cast<const uint4*>(qr + c * 8);
+    }
+  }
+
+  // ---- the first page's requests
   const int pg0 = pb + wave;
   PageRegs bufA, bufB;
   const int ph0 = phys_of(pg0);
@@ -304,8 +323,21 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
   uint32_t meta_b = load_meta(pg0 + 4, ph_b);
   load_coefs(ph0, bufA);
 
-  // ---- absorbed query: qt[h][i] = (row i of B^K, or U^K for i >= R) . q_h
-  for (int e = tid; e < NB * 4 * kW; e += 256) {
+  if (tid < NE) {
+    float acc = 0.f;
+    if (live0) {
+#pragma unroll
+      for (int c = 0; c < HD / 8; ++c) {
+        acc = dot2_bf16(x0[c].x, y0[c].x, acc);
+        acc = dot2_bf16(x0[c].y, y0[c].y, acc);
+        acc = dot2_bf16(x0[c].z, y0[c].z, acc);
+        acc = dot2_bf16(x0[c].w, y0[c].w, acc);
+      }
+    }
+    qt[e0h][e0i] = acc * a.scale_log2;
+  }
+  // further elements (more than 256 when G > 4)
+  for (int e = tid + 256; e < NE; e += 256) {
     const int h = e / kW, i = e % kW;
     float acc = 0.f;
     if (h < G) {
