@@ -60,7 +60,7 @@ typedef enum {
   KVS_ERR_NOT_SOURCE = 3,   /* map names a non-owner as source; append to a
                                layer that owns no cache entries                 */
   KVS_ERR_RANGE = 4,        /* count beyond cache capacity or workspace size    */
-  KVS_ERR_UNSUPPORTED = 5,  /* valid request this build does not implement
+  KVS_ERR_UNSUPPORTED = 5,  /* valid request the library does not implement
                                (an unsupported head_dim / group size / dtype /
                                rank combination)                                */
   KVS_ERR_ALIGN = 6,        /* a device pointer is not 16-byte aligned          */
