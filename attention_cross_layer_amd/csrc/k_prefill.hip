@@ -118,6 +118,23 @@ __device__ __forceinline__ uint4 mix_chunk(const uint4& a, const uint4& b, float
   return r;
 }
 
+// The bf16 remainder w0*a + w1*b - bf16(w0*a + w1*b) per element of two
+// 16-byte chunks (the mix in fp32, as mix_chunk forms it).
+__device__ __forceinline__ uint4 mix_chunk_rest(const uint4& a, const uint4& b, float w0, float w1) {
+  uint4 r;
+  const uint32_t* pa = &a.x;
+  const uint32_t* pb = &b.x;
+  uint32_t* pr = &r.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = fmaf(w0, dev::bf16_lo(pa[i]), w1 * dev::bf16_lo(pb[i]));
+    const float hi = fmaf(w0, dev::bf16_hi(pa[i]), w1 * dev::bf16_hi(pb[i]));
+    const uint32_t h = pack_bf16(lo, hi);
+    pr[i] = pack_bf16(lo - dev::bf16_lo(h), hi - dev::bf16_hi(h));
+  }
+  return r;
+}
+
 // Waves per workgroup.  Eight waves sharing each staged tile halve the
 // staging loads and LDS writes per MFMA against two 4-wave workgroups per CU
 // (hd 128: 395 vs 427 us per DepthGraft chunk layer; hd 64: 144 vs 159 us
@@ -139,6 +156,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][64 * HD];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][HD * kVRow];
+  // Two sources: the bf16 remainders of the mixed K and V^T tiles, so that
+  // both products see the fp32 mix to about 16 bits.  Rounding the mixed
+  // tiles to bf16 alone moved single outputs by up to 1e-2 where a few keys
+  // dominate a row (mostly through the scores), at the edge of the error
+  // bound; the remainders double the MFMAs of a two-source layer.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds_lo[NSRC == 2 ? 2 : 1][NSRC == 2 ? 64 * HD : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds_lo[NSRC == 2 ? 2 : 1][NSRC == 2 ? HD * kVRow : 8];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -221,6 +245,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
       const int key = KPP * j + kk, c = kWays * cc + w;
       uint4 v = NSRC == 2 ? mix_chunk(st.k[0][u], st.k[NSRC - 1][u], a.w0, a.w1) : st.k[0][u];
       *reinterpret_cast<uint4*>(&k_lds[buf][key * HD + ((c ^ (key & (NCH - 1))) * 8)]) = v;
+      if constexpr (NSRC == 2)
+        *reinterpret_cast<uint4*>(&k_lds_lo[buf][key * HD + ((c ^ (key & (NCH - 1))) * 8)]) =
+            mix_chunk_rest(st.k[0][u], st.k[1][u], a.w0, a.w1);
     }
     // V^T: this thread holds VCH consecutive key pairs of its 4 dims (a
     // dword = one dim of a key pair), so each dim row takes one VCH-dword
@@ -255,6 +282,33 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
 #pragma unroll
         for (int u = 0; u < VCH; ++u) row[swz16(k0 + 2 * u) / 2] = w[i][u];
       }
+      if constexpr (NSRC == 2) {
+        // the remainders, stored after the rounded mix to keep registers down
+#pragma unroll
+        for (int u = 0; u < VCH; ++u) {
+          const uint4 v = mix_chunk_rest(st.v[0][u], st.v[1][u], a.w0, a.w1);
+          w[0][u] = v.x;
+          w[1][u] = v.y;
+          w[2][u] = v.z;
+          w[3][u] = v.w;
+        }
+        if (!(page_ok && key0 + 64 <= T)) {
+#pragma unroll
+          for (int u = 0; u < VCH; ++u) {
+            const int k0 = key0 + 2 * (q * VCH + u);
+            const uint32_t mk = (page_ok && k0 < T ? 0x0000ffffu : 0u) | (page_ok && k0 + 1 < T ? 0xffff0000u : 0u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i][u] &= mk;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t* row = reinterpret_cast<uint32_t*>(&v_lds_lo[buf][0] + vrow_of(4 * L + i) * kVRow);
+          const int k0 = 2 * VCH * q;
+#pragma unroll
+          for (int u = 0; u < VCH; ++u) row[swz16(k0 + 2 * u) / 2] = w[i][u];
+        }
+      }
     }
   };
 
@@ -288,16 +342,23 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
         const int c = 2 * ks + hh;
         const uint4 kv = *reinterpret_cast<const uint4*>(&k_lds[buf][key * HD + ((c ^ (key & (NCH - 1))) * 8)]);
         s[kb] = mfma32(kv, qreg[ks], s[kb]);
+        if constexpr (NSRC == 2) {
+          const uint4 kl = *reinterpret_cast<const uint4*>(&k_lds_lo[buf][key * HD + ((c ^ (key & (NCH - 1))) * 8)]);
+          s[kb] = mfma32(kl, qreg[ks], s[kb]);
+        }
       }
     }
-    // the K operand reads run four ahead of the MFMAs that take them
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    // the K operand reads run four ahead of the MFMAs that take them (two
+    // ahead with two sources, whose tile stages hold twice the registers)
+    constexpr int NQK = 2 * KS * NSRC;        // score MFMAs (and K reads) per tile
+    constexpr int AHEAD = NSRC == 2 ? 2 : 4;
+    __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * KS - 4; ++i) {
+    for (int i = 0; i < NQK - AHEAD; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 
     // ---- online softmax for this lane's query row, on raw scores (the
     // positive scale commutes with the max); keys past the row's limit are
@@ -364,6 +425,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
         const int d = 32 * mb + col;
         const uint16_t* vrow = &v_lds[buf][vrow_of(d) * kVRow + 16 * sp + 8 * hh];
         o[mb] = mfma32(*reinterpret_cast<const uint4*>(vrow), pb[sp], o[mb]);
+        if constexpr (NSRC == 2) {
+          const uint16_t* vlo = &v_lds_lo[buf][vrow_of(d) * kVRow + 16 * sp + 8 * hh];
+          o[mb] = mfma32(*reinterpret_cast<const uint4*>(vlo), pb[sp], o[mb]);
+        }
       }
   };
   for (int t = 0; t < n_tiles; t += 2) {
@@ -413,6 +478,8 @@ PrefillFn pick_g(int G) {
     case 2: return run_prefill<HD, 2, NSRC>;
     case 4: return run_prefill<HD, 4, NSRC>;
     case 8: return run_prefill<HD, 8, NSRC>;
+    case 16: return run_prefill<HD, 16, NSRC>;
+    case 32: return run_prefill<HD, 32, NSRC>;
     default: return nullptr;
   }
 }

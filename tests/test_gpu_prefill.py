@@ -30,6 +30,12 @@ CASES = {
     "g8_hd64": (W["tinyllama_cla2"].with_(n_layers=2), 2, 520, [500, 333], 100, True),
     "g1_hd64": (W["tinyllama_cla2"].with_(n_layers=2, n_q_heads=4, n_kv_heads=4), 2, 192, [192, 70], 70, True),
     "g2_hd128_mixed": (W["depthgraft"].with_(n_layers=6, dg_stride=2, n_q_heads=16), 1, 150, [150], 33, True),
+    "g16_hd128": (W["cla2_64k"].with_(n_layers=2, n_q_heads=16, n_kv_heads=1), 2, 200, [200, 90], 90, True),
+    # one query head per KV head and few keys per early row, so single keys
+    # dominate rows: the mixed V tile must not be rounded to bf16 alone
+    "depthgraft_g1_hd128_few_keys": (W["cla2_64k"].with_(n_layers=6, n_q_heads=1, n_kv_heads=1, share="depthgraft",
+                                                         dg_stride=2), 2, 100, [97, 100], 77, True),
+    "g32_hd64": (W["tinyllama_cla2"].with_(n_layers=2, n_q_heads=32, n_kv_heads=1), 2, 140, [140, 75], 75, True),
 }
 
 
