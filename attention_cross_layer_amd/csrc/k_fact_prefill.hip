@@ -18,8 +18,10 @@
 //   workgroup = 4 waves on one KV head, each owning 32 query rows of one head
 //   (min(G, 4) heads x 4/min(G, 4) blocks of 32 positions), as the dense
 //   prefill.
-//   prologue  Q~^T = B^K Q^T and U~^T = [U^K; 0] Q^T (2 hd/16 MFMAs).  Their
-//             result registers serve as B operands unchanged: register r holds
+//   prologue  Q~^T = B^K Q^T and U~^T = [U^K; 0] Q^T (2 hd/16 MFMAs), each
+//             split into a bf16 high part and the bf16 rounding of the
+//             remainder.  Their result registers serve as B operands
+//             unchanged: register r holds
 //             coefficient 8(r/4) + 4(l/32) + r%4, so in every product over the
 //             coefficient space the k index visits coefficients in that order.
 //             Staged tiles store each 16-wide group with its quads 1 and 2
@@ -32,7 +34,8 @@
 //              C^V^T [32][64 keys], S^V^T = (s^V d^V)^T [16][64 keys]; keys
 //              past the sequence end, or on a corrupt page-table entry, are
 //              zero on the value side and have no codes.
-//     S^T = C^K Q~^T + S^K U~^T   6 MFMAs per wave
+//     S^T = C^K Q~^T + S^K U~^T   12 MFMAs per wave (high parts and
+//              remainders)
 //     softmax  online per query row, as the dense prefill
 //     A^T += C^V^T P^T, D^T += S^V^T P^T   8 MFMAs (rows 16..31 of the second
 //              product's A operand are zero)
@@ -282,7 +285,10 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
   }
   uint32_t meta_next = load_meta(1, ph_a);
 
-  uint4 bq[2], bu;
+  // Q~ and U~ as bf16 high parts and bf16 remainders: rounding them alone
+  // moved scores enough to take single outputs past 1e-2 where a few keys
+  // dominate a row
+  uint4 bq[2], bu, bq_lo[2], bu_lo;
   {
     const int qrow = row_ok ? row : (n - 1);
     const uint16_t* qp = a.q + (((size_t)b * n + qrow) * a.n_q_heads + head) * HD;
@@ -299,11 +305,8 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
       qu = mfma32(au, qv, qu);
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      bq[ks] = make_uint4(pack_bf16(qt[8 * ks + 0], qt[8 * ks + 1]), pack_bf16(qt[8 * ks + 2], qt[8 * ks + 3]),
-                          pack_bf16(qt[8 * ks + 4], qt[8 * ks + 5]), pack_bf16(qt[8 * ks + 6], qt[8 * ks + 7]));
-    bu = make_uint4(pack_bf16(qu[0], qu[1]), pack_bf16(qu[2], qu[3]), pack_bf16(qu[4], qu[5]),
-                    pack_bf16(qu[6], qu[7]));
+    for (int ks = 0; ks < 2; ++ks) split8(qt, 8 * ks, bq[ks], bq_lo[ks]);
+    split8(qu, 0, bu, bu_lo);
   }
 
   f32x16_t acc_c = f32x16_t{}, acc_d = f32x16_t{};
@@ -337,6 +340,9 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
       s[kb] = mfma32(c0, bq[0], f32x16_t{});
       s[kb] = mfma32(c1, bq[1], s[kb]);
       s[kb] = mfma32(dq, bu, s[kb]);
+      s[kb] = mfma32(c0, bq_lo[0], s[kb]);
+      s[kb] = mfma32(c1, bq_lo[1], s[kb]);
+      s[kb] = mfma32(dq, bu_lo, s[kb]);
     }
 
     // ---- online softmax for this lane's query row on raw scores

@@ -23,6 +23,10 @@ CASES = {
     "g1_hd64": (F.with_(n_layers=2, n_q_heads=2, n_kv_heads=2, head_dim=64), 2, 129, [129, 33], 33, True),
     "g2_hd128_top": (F.with_(n_layers=4, n_q_heads=4, n_kv_heads=2, share="pairs_top"), 2, 190,
                      [190, 70], 70, True),
+    # few keys per early row, so single keys dominate rows: the absorbed
+    # queries must not be rounded to bf16 alone
+    "g8_hd128_few_keys": (F.with_(n_layers=4, n_q_heads=64, n_kv_heads=8), 1, 500, [57], 50, True),
+    "g8_hd128_few_keys_full": (F.with_(n_layers=4, n_q_heads=64, n_kv_heads=8), 1, 500, [57], 50, False),
 }
 
 
