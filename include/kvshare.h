@@ -363,16 +363,18 @@ KVS_API kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cache,
  * sequence (their K/V already appended): query i of sequence b is at
  * P = seq_len[b] - n + i and sees keys 0..P when causal != 0 (inclusive
  * diagonal), else keys 0..seq_len[b]-1.  Query and key tiles go through bf16
- * MFMA with fp32 accumulation; a two-source layer's mixed K~/V~ tiles are
- * rounded to bf16 before the MFMA.
+ * MFMA with fp32 accumulation; a two-source layer's mixed K~/V~ tiles (mixed
+ * in fp32) enter the MFMA as their bf16 rounding plus the bf16 rounding of
+ * the remainder.
  *   q        device bf16 [batch][n][Hq][hd]
  *   seq_len  device int32 [batch], each >= n
  *   out      device [batch][n][Hq][hd] of out_dtype
  * Dense bf16 plans, and factorized plans (head_dim 64/128, ranks 32/16),
  * which attend in the coefficient space: q~ = B^K q and u~ = U^K q once per
  * query, scores c_t . q~ + s_t (d_t . u~), value accumulators in the 48
- * coefficients mapped back through B^V and U^V once per query row; q~, u~ and
- * the scaled codes s_t d_t enter the MFMA as bf16.  Other plans ->
+ * coefficients mapped back through B^V and U^V once per query row; q~ and u~
+ * enter the MFMA as a bf16 high part plus the bf16 remainder, the scaled
+ * codes s_t d_t as bf16.  Other plans ->
  * KVS_ERR_UNSUPPORTED. */
 KVS_API kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cache* cache,
                                           int32_t layer, const void* q, int32_t n,
