@@ -298,8 +298,8 @@ extern "C" kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cac
   }
   if (p.cfg.dtype != KVS_BF16)
     return fail(KVS_ERR_UNSUPPORTED, "prefill runs on bf16 caches (bf16 MFMA)");
-  if (!prefill_shape_supported(p.cfg.head_dim, group))
-    return fail(KVS_ERR_UNSUPPORTED, "no prefill kernel for this head_dim/group size");
+  if (!prefill_shape_supported(p.cfg.head_dim, group, li.n_src))
+    return fail(KVS_ERR_UNSUPPORTED, "no prefill kernel for this head_dim/group size/source count");
   if (!cache->k_pool || !cache->v_pool || !cache->page_table) return fail(KVS_ERR_ARG, "null cache pool");
   if (!aligned16(q) || !aligned16(out) || !aligned16(cache->k_pool) || !aligned16(cache->v_pool) ||
       !aligned4(seq_len) || !aligned4(cache->page_table))

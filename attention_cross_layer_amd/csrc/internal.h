@@ -106,7 +106,7 @@ struct AppendLaunch {
 };
 int launch_append(const AppendLaunch& a, void* stream);
 
-bool prefill_shape_supported(int32_t head_dim, int32_t group);
+bool prefill_shape_supported(int32_t head_dim, int32_t group, int32_t n_src);
 
 struct PrefillLaunch {
   const void* k_pool;

@@ -47,7 +47,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace kvs {

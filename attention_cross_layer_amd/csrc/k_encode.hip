@@ -42,7 +42,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace kvs {

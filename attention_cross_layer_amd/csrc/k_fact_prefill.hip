@@ -47,7 +47,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace kvs {
@@ -316,6 +316,9 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     const int ph_c = phys_of(t + 3);
+    // a page-table entry outside [0, n_phys_pages) (uniform): its keys get no
+    // weight, as the decode skips such a page
+    const bool tile_ok = ph_r >= 0;
     store_tile(t, buf);
     {
       const uint32_t m1 = meta_next;
@@ -346,13 +349,14 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
     }
 
     // ---- online softmax for this lane's query row on raw scores
-    if (t >= unmasked_tiles) {
+    if (t >= unmasked_tiles || !tile_ok) {
+      const int lim = tile_ok ? row_kend : 0;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = t * 64 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
-          s[kb][r] = key < row_kend ? s[kb][r] : -INFINITY;
+          s[kb][r] = key < lim ? s[kb][r] : -INFINITY;
         }
     }
     float mt = -INFINITY;

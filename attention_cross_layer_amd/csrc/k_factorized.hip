@@ -48,7 +48,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace kvs {
@@ -390,8 +390,10 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
     for (int m = 0; m < 12; ++m) acc[hb][m] = f4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  auto compute = [&](int pg, const PageRegs& r) {
-    const int nvalid = n_keys - pg * kPage;
+  // ph < 0 here: the page's table entry is out of range; its keys get no
+  // weight (its loads returned zeros)
+  auto compute = [&](int pg, int ph, const PageRegs& r) {
+    const int nvalid = ph >= 0 ? n_keys - pg * kPage : 0;
     const bool tail = nvalid < kPage;
     // score A operands of the codes (token = lane)
     uint32_t ad[4][2];
@@ -523,18 +525,21 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
   // ---- main loop over this wave's pages pg0, pg0+4, ...: two page buffers,
   // the next page's loads issued before the current page is computed, the
   // page after next's meta one step earlier still
+  int ph_in_a = ph0;
   for (int pg = pg0; pg < pe; pg += 8) {
     const int ph_c = phys_of(pg + 8);
     const uint32_t meta_c = load_meta(pg + 8, ph_c);
+    const int ph_in_b = ph_b;
     load_coefs(ph_b, bufB);
     load_codes(ph_b, meta_b, bufB);
-    compute(pg, bufA);
+    compute(pg, ph_in_a, bufA);
     if (pg + 4 >= pe) break;
     ph_b = phys_of(pg + 12);
     meta_b = load_meta(pg + 12, ph_b);
+    ph_in_a = ph_c;
     load_coefs(ph_c, bufA);
     load_codes(ph_c, meta_c, bufA);
-    compute(pg + 4, bufB);
+    compute(pg + 4, ph_in_b, bufB);
   }
 
   // ---- this wave's per-head (coefficient sums, m, l) to LDS

@@ -9,9 +9,11 @@
 // reusing layers read the source layer's K/V).  A two-source layer reads the
 // DepthGraft mix K~ = w0 K_s0 + w1 K_s1 ("DepthGraft: Structural
 // Regularization through Hierarchical Cross-Layer KV Reconstruction",
-// Abstract), formed in fp32 while a tile is staged and rounded to bf16 for
-// the MFMA.  DepthGraft's owner layers are the only ones that need prefill
-// for all prompt tokens (the Abstract's "prefill early completion").
+// Abstract), formed in fp32 while a tile is staged and carried into the
+// MFMA as two bf16 tiles, the rounded mix and the rounding of its remainder
+// (about 16 significant bits), so both products run twice for such a layer.
+// DepthGraft's owner layers are the only ones that need prefill for all
+// prompt tokens (the Abstract's "prefill early completion").
 //
 // Decomposition (gfx950, v_mfma_f32_32x32x16_bf16; lane l of A/B holds row or
 // column l%32 and k = 8*(l/32)+e; result register r of lane l is row
@@ -41,7 +43,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace kvs {
@@ -221,7 +223,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
   auto v_chunk = [&](int u) { return ((tid / (HD / 4)) * VCH + u) * (HD / 4) + tid % (HD / 4); };
   auto load_tile = [&](int entry, Stage& st) {
     st.entry = entry;
-    const int page = (unsigned)entry < (unsigned)a.n_phys_pages ? entry : 0;   // corrupt entry: read page 0, masked below
+    // an entry outside [0, n_phys_pages) reads page 0 in its place; store_tile
+    // zeroes that tile's values and tile_step gives its keys no weight, so the
+    // keys of such a page are skipped, as the decode skips them
+    const int page = (unsigned)entry < (unsigned)a.n_phys_pages ? entry : 0;
     const int64_t tile = ((int64_t)page * a.n_kv_heads + kvh) * (64 * HD);
 #pragma unroll
     for (int s = 0; s < NSRC; ++s) {
@@ -327,6 +332,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
   auto tile_step = [&](int t, Stage& st) {
     const int buf = t & 1;
     const int pt_b = pt[min(t + 3, n_tiles - 1)];
+    const bool tile_ok = (unsigned)st.entry < (unsigned)a.n_phys_pages;   // uniform
     store_tile(t, st.entry, buf, st);
     if (t + 2 < n_tiles) load_tile(pt_a, st);
     pt_a = pt_b;
@@ -362,14 +368,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
 
     // ---- online softmax for this lane's query row, on raw scores (the
     // positive scale commutes with the max); keys past the row's limit are
-    // masked only in tiles that reach a limit
-    if (t >= unmasked_tiles) {
+    // masked only in tiles that reach a limit, and every key of a tile whose
+    // page-table entry is out of range
+    if (t >= unmasked_tiles || !tile_ok) {
+      const int lim = tile_ok ? row_kend : 0;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = t * 64 + 32 * kb + 8 * (r / 4) + 4 * hh + (r % 4);
-          s[kb][r] = key < row_kend ? s[kb][r] : -INFINITY;
+          s[kb][r] = key < lim ? s[kb][r] : -INFINITY;
         }
     }
     float mt = -INFINITY;
@@ -471,6 +479,9 @@ int run_prefill(PrefillParams p, int B, hipStream_t st, const KernelEvents& ev) 
 
 typedef int (*PrefillFn)(PrefillParams, int, hipStream_t, const KernelEvents&);
 
+// Group sizes a plan can reach: the decode kernels take two sources up to
+// G = 8 and one source up to G = 16 (G = 32 at hd 64 only), so the prefill
+// is built for the same shapes and no others.
 template <int HD, int NSRC>
 PrefillFn pick_g(int G) {
   switch (G) {
@@ -478,8 +489,12 @@ PrefillFn pick_g(int G) {
     case 2: return run_prefill<HD, 2, NSRC>;
     case 4: return run_prefill<HD, 4, NSRC>;
     case 8: return run_prefill<HD, 8, NSRC>;
-    case 16: return run_prefill<HD, 16, NSRC>;
-    case 32: return run_prefill<HD, 32, NSRC>;
+    case 16:
+      if constexpr (NSRC == 1) return run_prefill<HD, 16, 1>;
+      return nullptr;
+    case 32:
+      if constexpr (NSRC == 1 && HD == 64) return run_prefill<64, 32, 1>;
+      return nullptr;
     default: return nullptr;
   }
 }
@@ -492,8 +507,8 @@ PrefillFn pick(int hd, int G, int nsrc) {
 
 }  // namespace
 
-bool prefill_shape_supported(int32_t head_dim, int32_t group) {
-  return pick(head_dim, group, 1) != nullptr;
+bool prefill_shape_supported(int32_t head_dim, int32_t group, int32_t n_src) {
+  return pick(head_dim, group, n_src) != nullptr;
 }
 
 int launch_prefill(const PrefillLaunch& a, void* stream) {

@@ -13,7 +13,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "common.cuh"
+#include "common.h"
 #include "internal.h"
 
 namespace kvs {

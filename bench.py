@@ -6,24 +6,38 @@ then every layer runs split-K decode attention over its source slot(s)
 (kvs_attn_decode: the partition kernel, plus a small merge kernel when the
 sequence is split into several partitions).  The factorized workload
 appends the new token's coefficients, codes, scales and rank
-(kvs_append_factorized) instead of K/V.  Inputs are
-resident in HBM before the timed region; K/V and queries are seeded
-synthetic N(0,1) tensors of the workload's shapes.
+(kvs_append_factorized) instead of K/V.  Inputs are resident in HBM before
+the timed region; K/V and queries are seeded synthetic N(0,1) tensors of
+the workload's shapes.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--roofline-only] [--no-cpu-baseline]
+                    [--roofline-only] [--no-cpu-baseline] [--no-extras]
+    python bench.py --sweep [--sweep-out FILE]
 
+The default workload is the long-context decode: 32 layers, CLA2 map, batch
+4, context 65536, 32 q / 8 KV heads, head_dim 128, bf16, 1% of keys x4.
 Prints one JSON line.  ``value`` is decode tokens/s (one token per sequence
-per step, warm back-to-back steps).  ``roofline`` rates the decode launch of
-a single-source layer against the 8 TB/s HBM peak with its algorithmic bytes
-(every source tile, K and V, read once): its duration is timed with a pair
-of HIP events that the library attaches to the decode kernel's own start and
-end (kvs_time_next_launch, i.e. hipExtLaunchKernel; the partition merge and
-the launch latency are reported apart as avg_call_us), with the 256 MB
-Infinity Cache flushed before each launch by reading a 512 MB buffer (a read
-leaves no dirty lines whose write-back would compete with the timed launch),
-so no byte of the timed launch is served from a cache.
-``cpu_baseline`` times the fp64 oracle on a bounded sample of sequences.
+per step, warm back-to-back steps); ``ms_per_step_cold`` is the same step
+with the 256 MB Infinity Cache flushed before every layer's calls (the
+flush itself outside the timed intervals).  ``roofline`` rates the decode
+launch of a single-source layer against the 8 TB/s HBM peak with its
+algorithmic bytes (every source tile, K and V, read once): its duration is
+timed with a pair of HIP events that the library attaches to the decode
+kernel's own start and end (kvs_time_next_launch, i.e. hipExtLaunchKernel;
+the partition merge and the launch latency are reported apart as
+avg_call_us), with the cache flushed before each launch by reading a 512 MB
+buffer (a read leaves no dirty lines whose write-back would compete with
+the timed launch), so no byte of the timed launch is served from a cache.
+``cpu_baseline`` times the fp64 oracle (one BLAS thread) on a bounded
+sample of the same workload, scaled to the metric's unit.  The default run
+adds the 64K factorized decode (``roofline_factorized``, with its own CPU
+baseline) and the 4-layer fp32 toy step's time (``tiny_cla2``).
+
+``--sweep`` times the metric's batch x context grid: the 1.1B-shaped CLA2
+decode at B in {1, 8, 16, 32, 64, 128} x ctx in {512, 1024, 2048} and the
+long-context CLA2 decode at B in {1, 2, 4, 8} x ctx in {16K, 32K, 64K}:
+tokens/s and HBM rates of the warm step, the cold step and the cache-flushed
+kernel; one JSON line, and a markdown table with --sweep-out.
 """
 import argparse
 import json
@@ -42,6 +56,8 @@ import datagen  # noqa: E402
 METRIC = "shared-KV decode attn: tokens/s and achieved HBM GB/s (% of peak) per batch x ctx"
 HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20
+DEFAULT_WORKLOAD = "cla2_64k"
+CPU_BUDGET_S = 12.0
 
 
 def log(msg):
@@ -123,28 +139,190 @@ def fact_bytes_per_call(wl, rank):
     return wl.n_kv_heads * (tokens * (2 * wl.basis_rank * 2 + 4) + 2 * sum_r) + tokens
 
 
-def cpu_baseline(wl, src, w, host_seq, budget_s=12.0):
-    """fp64 oracle, single-threaded BLAS, over whole decode steps (all layers)
-    of one sequence after another (cycling through the batch) until about
-    ``budget_s`` of CPU time."""
+
+# ----------------------------------------------------------------------------
+# the oracle timed on the host: one BLAS thread, a bounded sample of the
+# workload's units, inputs prepared outside the timed region, the oracle's
+# own bf16/fp16/int8 -> fp64 upcast inside it
+# ----------------------------------------------------------------------------
+
+def oracle_time(prep, run, budget_s):
+    """Call run(*prep(i)) for i = 0, 1, ... until ``budget_s`` seconds of
+    timed run() calls; returns (calls, seconds)."""
     from threadpoolctl import threadpool_limits
 
-    from oracle import attention as A
-
-    done = 0
-    elapsed = 0.0
+    done, elapsed = 0, 0.0
     with threadpool_limits(limits=1):
         while elapsed < budget_s:
-            kk, vv, qs = host_seq(done % wl.batch)
+            args = prep(done)
             t0 = time.perf_counter()
-            for l in range(wl.n_layers):
-                A.layer_decode(src.tolist(), w.tolist(), l, kk, vv, qs[l], [wl.ctx])
+            run(*args)
             elapsed += time.perf_counter() - t0
             done += 1
-    return {"value": done / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} sequence decode steps (cycling through the {wl.batch} sequences), "
-                      f"each over all {wl.n_layers} layers at ctx {wl.ctx}, {elapsed:.1f} s "
-                      f"(bf16->fp64 upcast included)"}
+    return done, elapsed
+
+
+def cpu_dense_decode(rig, budget_s=CPU_BUDGET_S):
+    """Oracle decode of whole layer calls of one sequence after another
+    (layers in order, then the next sequence): effective K/V of the layer's
+    sources, then attention over every key.  Rate in tokens/s = sequence
+    steps (L layer calls each) per second."""
+    from oracle import attention as A
+
+    wl, L = rig.wl, rig.wl.n_layers
+    src, w = rig.src.tolist(), rig.w.tolist()
+    host, cur = {}, [-1]
+
+    def prep(i):
+        b, l = (i // L) % wl.batch, i % L
+        if b != cur[0]:
+            host.clear()
+            cur[0] = b
+        for s in (int(x) for x in rig.src[l] if int(x) >= 0):
+            if s not in host:
+                k, v = datagen.owner_kv(wl, s, device="cuda")
+                k[:, wl.ctx - 1:] = rig.new_kv[s][0]
+                v[:, wl.ctx - 1:] = rig.new_kv[s][1]
+                host[s] = (k[b:b + 1].cpu(), v[b:b + 1].cpu())
+                del k, v
+        return l, rig.qs[l][b:b + 1].cpu()
+
+    def run(l, q):
+        A.layer_decode(src, w, l, {s: kv[0] for s, kv in host.items()},
+                       {s: kv[1] for s, kv in host.items()}, q, [wl.ctx])
+
+    done, el = oracle_time(prep, run, budget_s)
+    return {"value": done / L / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} layer calls ({done / L:.2f} sequence decode steps of {L} layers) at "
+                      f"ctx {wl.ctx}, sequences taken in turn, {el:.1f} s; rate = sequence steps/s; "
+                      f"bf16->fp64 upcast included"}
+
+
+def cpu_fact_decode(rig, budget_s=CPU_BUDGET_S):
+    """Oracle decode over the factorized cache: every key and value of the
+    layer rebuilt from its coefficients, basis, scaled codes and residual
+    directions (the plain definition), then attention; layer calls of one
+    sequence after another."""
+    from oracle import attention as A
+
+    wl, L = rig.wl, rig.wl.n_layers
+    T = wl.ctx
+    one_b = {}
+
+    def host_layer(b, l):
+        o = int(rig.src[l, 0])
+        ck, cv = datagen.pair_coeffs(wl, o // 2, device="cuda")
+        bk, bv = datagen.pair_basis(wl, o // 2, device="cuda")
+        uk, uv = datagen.layer_residual_basis(wl, l, device="cuda")
+        dk, dv, sk, sv = datagen.layer_residual(wl, l, rig.rank, device="cuda")
+        nf_o, nf_l = rig.new_f[o], rig.new_f[l]
+        ck[:, T - 1:], cv[:, T - 1:] = nf_o[0], nf_o[1]
+        dk[:, T - 1:], dv[:, T - 1:], sk[:, T - 1:], sv[:, T - 1:] = nf_l[2], nf_l[3], nf_l[4], nf_l[5]
+        sl = slice(b, b + 1)
+        return tuple(x[sl].cpu() for x in (ck, cv, dk, dv, sk, sv)) + (
+            bk.cpu(), bv.cpu(), uk.cpu(), uv.cpu(), rig.rank[sl].cpu())
+
+    def prep(i):
+        b, l = (i // L) % wl.batch, i % L
+        one_b.clear()
+        one_b["x"] = host_layer(b, l)
+        return l, rig.qs[l][b:b + 1].cpu()
+
+    def run(l, q):
+        ck, cv, dk, dv, sk, sv, bk, bv, uk, uv, r = one_b["x"]
+        kk = A.factorized_kv(ck, bk, sk, dk, uk, r)
+        vv = A.factorized_kv(cv, bv, sv, dv, uv, r)
+        A.attend_decode(q, kk, vv, [T])
+
+    done, el = oracle_time(prep, run, budget_s)
+    return {"value": done / L / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} layer calls ({done / L:.2f} sequence decode steps of {L} layers) at "
+                      f"ctx {T}: every key/value rebuilt from the factorized entries, then "
+                      f"attention, {el:.1f} s; rate = sequence steps/s"}
+
+
+def cpu_prefill(wl, layers, host_kv, qs, n, budget_s=CPU_BUDGET_S):
+    """Oracle causal prefill chunk, one (layer, query head) at a time: that
+    head's n queries over the keys of its KV head.  The step time is the
+    mean time per (layer, head) times heads x layers."""
+    from oracle import attention as A
+
+    G, T, Hq = wl.group, wl.ctx, wl.n_q_heads
+    units = [(l, h) for l in layers for h in range(Hq)]
+
+    def prep(i):
+        l, h = units[i % len(units)]
+        k, v = host_kv(l)
+        g = h // G
+        return qs[l][:, :, h:h + 1], k[:, :, g:g + 1], v[:, :, g:g + 1]
+
+    def run(q, k, v):
+        A.attend_prefill(q, k, v, [T], causal=True)
+
+    done, el = oracle_time(prep, run, budget_s)
+    step_s = el / done * Hq * len(layers)
+    return {"value": n / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} (layer, query head) units of the {n}-query causal chunk over {T} keys "
+                      f"in {el:.1f} s, scaled by {Hq} heads x {len(layers)} layers "
+                      f"= {Hq * len(layers) / done:.1f}x the timed sample"}
+
+
+def cpu_fact_prefill(wl, layers, host_layer, qs, n, budget_s=CPU_BUDGET_S):
+    """Oracle causal prefill over the factorized cache, one (layer, KV head)
+    at a time: that head's keys and values rebuilt from the factorized
+    entries, then the G query heads' chunk attention over them."""
+    from oracle import attention as A
+
+    G, T, Hkv = wl.group, wl.ctx, wl.n_kv_heads
+    units = [(l, g) for l in layers for g in range(Hkv)]
+
+    def prep(i):
+        l, g = units[i % len(units)]
+        ck, cv, dk, dv, sk, sv, bk, bv, uk, uv, r = host_layer(l)
+        hs = slice(g, g + 1)
+        return (l, g, ck[:, :, hs], cv[:, :, hs], dk[:, :, hs], dv[:, :, hs], sk[:, :, hs],
+                sv[:, :, hs], bk[hs], bv[hs], uk[hs], uv[hs], r)
+
+    def run(l, g, ck, cv, dk, dv, sk, sv, bk, bv, uk, uv, r):
+        kk = A.factorized_kv(ck, bk, sk, dk, uk, r)
+        vv = A.factorized_kv(cv, bv, sv, dv, uv, r)
+        for h in range(g * G, (g + 1) * G):
+            A.attend_prefill(qs[l][:, :, h:h + 1], kk, vv, [T], causal=True)
+
+    done, el = oracle_time(prep, run, budget_s)
+    step_s = el / done * Hkv * len(layers)
+    return {"value": n / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} (layer, KV head) units (rebuild of that head's {T} keys/values, then "
+                      f"its {G} query heads' {n}-query causal chunk) in {el:.1f} s, scaled by "
+                      f"{Hkv} KV heads x {len(layers)} layers = {Hkv * len(layers) / done:.1f}x"}
+
+
+def cpu_encode(wl, n, rows, owner_of, bases, rank, budget_s=CPU_BUDGET_S):
+    """Oracle encoder over whole layers: coefficients from the slot owner's
+    rows, residual coordinates on the layer's directions, fp16 scale and
+    int8 codes at each token's rank, for K and V."""
+    from oracle import factorize as F
+
+    L = wl.n_layers
+
+    def prep(i):
+        l = i % L
+        o = owner_of(l)
+        bk, bv, uk, uv = bases(l)
+        return (rows[l][0].cpu(), rows[o][0].cpu(), rows[l][1].cpu(), rows[o][1].cpu(),
+                bk.cpu(), bv.cpu(), uk.cpu(), uv.cpu(), rank.cpu())
+
+    def run(k, ko, v, vo, bk, bv, uk, uv, r):
+        F.encode(k, ko, bk, uk, r)
+        F.encode(v, vo, bv, uv, r)
+
+    done, el = oracle_time(prep, run, budget_s)
+    step_s = el / done * L
+    return {"value": n / step_s, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} layers of the {n}-token chunk encoded (K and V) in {el:.1f} s, "
+                      f"scaled to {L} layers ({L / done:.1f}x the timed sample)"}
+
+
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
@@ -366,6 +544,8 @@ def prefill_kernel_flops(wl, kernel):
     return prefill_flops(wl.prefill_n, wl.ctx, wl.n_q_heads, wl.head_dim)
 
 
+
+
 def prefill_main(args, workload):
     """Prefill-chunk attention over one chunk per layer that needs it.
 
@@ -476,6 +656,30 @@ def prefill_main(args, workload):
     if traffic is not None:
         res["roofline"]["traffic"] = traffic["bytes_per_launch"]
         res["roofline"]["traffic_source"] = traffic["source"]
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline")
+        hq = {l: qs[l].cpu() for l in layers}
+        memo = {}
+        if fact:
+            def host_layer(l):
+                if l not in memo:
+                    memo.clear()
+                    o = int(src[l, 0])
+                    ck, cv = datagen.pair_coeffs(wl, o // 2, device="cuda")
+                    bk, bv = datagen.pair_basis(wl, o // 2, device="cuda")
+                    uk, uv = datagen.layer_residual_basis(wl, l, device="cuda")
+                    dk, dv, sk, sv = datagen.layer_residual(wl, l, rank, device="cuda")
+                    memo[l] = tuple(x.cpu() for x in (ck, cv, dk, dv, sk, sv, bk, bv, uk, uv, rank))
+                return memo[l]
+            res["cpu_baseline"] = cpu_fact_prefill(wl, layers, host_layer, hq, n)
+        else:
+            def host_kv(l):
+                if l not in memo:
+                    memo.clear()
+                    k, v = datagen.owner_kv(wl, l, device="cuda")
+                    memo[l] = (k.cpu(), v.cpu())
+                return memo[l]
+            res["cpu_baseline"] = cpu_prefill(wl, layers, host_kv, hq, n)
     print(json.dumps(res), flush=True)
 
 
@@ -609,7 +813,342 @@ def encode_main(args):
            "basis_build_ms": basis_ms,
            "basis_build": f"{len(owners)} pair bases + {wl.n_layers} residual bases "
                           f"(K and V) from {n} rows per layer, two batched calls"}
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline")
+
+        def bases(l):
+            s = owners.index(owner_of(l))
+            return bk[s], bv[s], uk[l], uv[l]
+        res["cpu_baseline"] = cpu_encode(wl, n, rows, owner_of, bases, rank)
     print(json.dumps(res), flush=True)
+
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+
+class DecodeRig:
+    """A workload's cache filled to its capacity (wl.batch sequences of
+    wl.ctx tokens), its queries, and the new token each step appends at
+    position ctx-1 of every sequence it runs.  Steps may run fewer sequences
+    (the first B) and a shorter context (positions 0..ctx-1)."""
+
+    def __init__(self, wl):
+        self.wl = wl
+        self.fact = wl.kind == "factorized"
+        if self.fact:
+            self.src, self.w, self.plan, self.cache, self.owners, self.rank = setup_factorized(wl)
+        else:
+            self.src, self.w, self.plan, self.cache, self.owners = setup(wl)
+        L = wl.n_layers
+        self.qs = [datagen.decode_q(wl, l, device="cuda") for l in range(L)]
+        self.stream = torch.cuda.current_stream()
+        if self.fact:
+            one = wl.with_(ctx=1)
+            r1 = self.rank[:, wl.ctx - 1:].contiguous()
+            self.r1 = r1
+            self.new_f = {}
+            for l in range(L):
+                cc = (datagen.pair_coeffs(one, 1000 + l, device="cuda") if l in self.owners
+                      else (None, None))
+                self.new_f[l] = cc + datagen.layer_residual(one, 1000 + l, r1, device="cuda")
+        else:
+            self.new_kv = {l: datagen.owner_kv(wl, 1000 + l, device="cuda", ctx=1) for l in self.owners}
+        self.flush = torch.ones((FLUSH_BYTES // 4 // 4096, 4096), dtype=torch.float32, device="cuda")
+
+    def call_bytes(self, l, B, ctx):
+        wl = self.wl
+        if self.fact:
+            return fact_bytes_per_call(wl.with_(batch=B, ctx=ctx), self.rank[:B, :ctx])
+        return bytes_per_call(wl.with_(batch=B, ctx=ctx), self.src, l)
+
+    def point(self, B, ctx):
+        """Callables and buffers of a step at batch B, context ctx."""
+        wl, st = self.wl, self.stream
+        L = wl.n_layers
+        pos = torch.full((B,), ctx - 1, dtype=torch.int32, device="cuda")
+        seq_len = torch.full((B,), ctx, dtype=torch.int32, device="cuda")
+        n_splits = K.kvs_decode_splits(self.plan, B, ctx)
+        ws = torch.zeros(K.kvs_decode_workspace_size(self.plan, B, n_splits), dtype=torch.uint8,
+                         device="cuda")
+        outs = [torch.empty((B, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
+                for _ in range(L)]
+        qs = [q[:B].contiguous() for q in self.qs]
+        if self.fact:
+            r1 = self.rank[:B, ctx - 1:ctx].contiguous()
+            new = {l: tuple(None if x is None else x[:B].contiguous() for x in v)
+                   for l, v in self.new_f.items()}
+
+            def append(l):
+                ck, cv, dk, dv, sk, sv = new[l]
+                K.kvs_append_factorized(self.plan, self.cache, l, ck, cv, dk, dv, sk, sv, r1, pos,
+                                        stream=st)
+        else:
+            new = {l: (kv[0][:B].contiguous(), kv[1][:B].contiguous()) for l, kv in self.new_kv.items()}
+
+            def append(l):
+                if l in new:
+                    K.kvs_append(self.plan, self.cache, l, new[l][0], new[l][1], pos, stream=st)
+
+        def decode(l):
+            K.kvs_attn_decode(self.plan, self.cache, l, qs[l], seq_len, ctx, out=outs[l],
+                              n_splits=n_splits, workspace=ws, stream=st)
+
+        return dict(append=append, decode=decode, n_splits=n_splits, qs=qs, seq_len=seq_len,
+                    outs=outs, ws=ws)
+
+    def warm_step_ms(self, pt, steps, warmup):
+        L, st = self.wl.n_layers, self.stream
+
+        def step():
+            for l in range(L):
+                pt["append"](l)
+                pt["decode"](l)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(st)
+        for _ in range(steps):
+            step()
+        t1.record(st)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    def cold_step_ms(self, pt, passes):
+        """A step with the cache flushed before each layer's calls: the sum of
+        the per-layer intervals (append + decode), the flushes outside them."""
+        L, st = self.wl.n_layers, self.stream
+        ev = []
+        for _ in range(passes):
+            for l in range(L):
+                self.flush.sum(dim=0)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                pt["append"](l)
+                pt["decode"](l)
+                e1.record(st)
+                ev.append((e0, e1))
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / passes
+
+    def launches(self, pt, layers, passes):
+        """Cache-flushed decode launches of ``layers``: per-launch kernel time
+        (events on the partition kernel) and call time (stream events)."""
+        st = self.stream
+        pt["decode"](layers[0])                      # warm the launch path
+        ev = []
+        for _ in range(passes):
+            for l in layers:
+                self.flush.sum(dim=0)
+                e0, e1, k0, k1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+                K.kvs_time_next_launch(k0, k1, st)
+                e0.record(st)
+                pt["decode"](l)
+                e1.record(st)
+                ev.append((l, e0, e1, k0, k1))
+        torch.cuda.synchronize()
+        kern = [k0.elapsed_time(k1) * 1e3 for _, e0, e1, k0, k1 in ev]
+        call = [e0.elapsed_time(e1) * 1e3 for _, e0, e1, k0, k1 in ev]
+        return sum(kern) / len(kern), sum(call) / len(call), len(ev)
+
+    def release(self):
+        del self.cache, self.flush, self.qs
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def decode_result(rig, args, cpu=True, step=True):
+    """Warm and cold steps, the flushed per-launch roofline of the dominant
+    kernel, and the oracle's CPU baseline for one decode workload."""
+    wl = rig.wl
+    L, B, ctx = wl.n_layers, wl.batch, wl.ctx
+    src = rig.src
+    pt = rig.point(B, ctx)
+    res = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+           "data": "synthetic", "config": describe(wl, src) | {"n_splits": pt["n_splits"]}}
+    step_bytes = sum(rig.call_bytes(l, B, ctx) for l in range(L))
+    if step:
+        ms = rig.warm_step_ms(pt, args.steps, args.warmup)
+        ms_cold = rig.cold_step_ms(pt, passes=2)
+        res |= {"value": B * 1000.0 / ms, "ms_per_step": ms,
+                "step_hbm_gbs": step_bytes / (ms * 1e-3) / 1e9,
+                "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "ms_per_step_cold": ms_cold,
+                "value_cold": B * 1000.0 / ms_cold,
+                "step_hbm_frac_cold": step_bytes / (ms_cold * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "step_bytes": step_bytes}
+    single = [l for l in range(L) if int(src[l, 1]) < 0]
+    mixed = [l for l in range(L) if int(src[l, 1]) >= 0]
+    dom = single if single else mixed
+    us, call_us, n = rig.launches(pt, dom, args.roofline_passes)
+    nbytes = rig.call_bytes(dom[0], B, ctx)
+    achieved = nbytes / (us * 1e-6) / 1e9
+    res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                       "kernel": ("fact_decode_kernel (factorized cache, split-K partitions)"
+                                  if rig.fact else
+                                  decode_kernel_name(wl, not single) + ", "
+                                  + ("single-source layer" if single else "two-source layer")),
+                       "bytes_per_launch": nbytes, "avg_launch_us": us,
+                       "timing": "HIP events on the kernel's own start and end (hipExtLaunchKernel)",
+                       "avg_call_us": call_us, "launches": n, "cache": "flushed"}
+    if single and mixed:
+        us2, call2, _ = rig.launches(pt, mixed, args.roofline_passes)
+        b2 = rig.call_bytes(mixed[0], B, ctx)
+        res["roofline_two_source"] = {"achieved": b2 / (us2 * 1e-6) / 1e9,
+                                      "frac": b2 / (us2 * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                      "bytes_per_launch": b2, "avg_launch_us": us2,
+                                      "avg_call_us": call2}
+    if rig.fact and step:
+        res["router"] = router_result(rig, pt, dom, args, us, call_us)
+    traffic = recorded_traffic(wl.name)
+    if traffic is not None:
+        res["roofline"]["traffic"] = traffic["bytes_per_launch"]
+        res["roofline"]["traffic_source"] = traffic["source"]
+    if cpu:
+        log(f"[bench] cpu baseline: {wl.name}")
+        res["cpu_baseline"] = cpu_fact_decode(rig) if rig.fact else cpu_dense_decode(rig)
+    return res
+
+
+def router_result(rig, pt, dom, args, us, call_us):
+    """Router statistics: the same cache-flushed launches with the entropy and
+    peak side output, then the rank choice over every layer's statistics."""
+    wl, st = rig.wl, rig.stream
+    L, B = wl.n_layers, wl.batch
+    stats = torch.empty((L, B, wl.n_q_heads, 2), dtype=torch.float32, device="cuda")
+    ev_s = []
+    for _ in range(args.roofline_passes):
+        for l in dom:
+            rig.flush.sum(dim=0)
+            e0, e1, k0, k1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
+            K.kvs_time_next_launch(k0, k1, st)
+            e0.record(st)
+            K.kvs_attn_decode_stats(rig.plan, rig.cache, l, pt["qs"][l], pt["seq_len"], wl.ctx,
+                                    out=pt["outs"][l], stats=stats[l], n_splits=pt["n_splits"],
+                                    workspace=pt["ws"], stream=st)
+            e1.record(st)
+            ev_s.append((e0, e1, k0, k1))
+    router = K.kvs_router(0.5, 0.8, 0.5, wl.resid_rank_max, wl.resid_rank_max // 2, 0)
+    ranks = torch.empty(B, dtype=torch.uint8, device="cuda")
+    K.kvs_route_ranks(rig.plan, stats, pt["seq_len"], router, rank_out=ranks, stream=st)
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(st)
+    for _ in range(10):
+        K.kvs_route_ranks(rig.plan, stats, pt["seq_len"], router, rank_out=ranks, stream=st)
+    r1.record(st)
+    torch.cuda.synchronize()
+    us_s = sum(k0.elapsed_time(k1) for e0, e1, k0, k1 in ev_s) * 1e3 / len(ev_s)
+    call_s = sum(e0.elapsed_time(e1) for e0, e1, k0, k1 in ev_s) * 1e3 / len(ev_s)
+    return {"decode_with_stats_us": us_s, "decode_us": us, "stats_overhead_frac": us_s / us - 1.0,
+            "call_with_stats_us": call_s, "call_us": call_us,
+            "stats_overhead_call_frac": call_s / call_us - 1.0,
+            "route_us": r0.elapsed_time(r1) * 1e3 / 10, "route_sets": L,
+            "routed_ranks": ranks.cpu().tolist()}
+
+
+def decode_main(args):
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path is a "
+              "single-GPU kernel library; sharding across GPUs is described, not built.",
+              file=sys.stderr)
+        sys.exit(2)
+    wl = datagen.WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    log(f"[bench] setting up {wl.name}")
+    rig = DecodeRig(wl)
+    if args.roofline_only:
+        res = decode_result(rig, args, cpu=False, step=False)
+        rig.release()
+        calibration_copy()
+        print(json.dumps(res), flush=True)
+        return
+    res = decode_result(rig, args, cpu=not args.no_cpu_baseline)
+    rig.release()
+    del rig
+    if args.workload == DEFAULT_WORKLOAD and not args.no_extras:
+        # the 64K factorized decode beside the dense one
+        log("[bench] setting up factorized_64k")
+        frig = DecodeRig(datagen.WORKLOADS["factorized_64k"])
+        f = decode_result(frig, args, cpu=not args.no_cpu_baseline)
+        frig.release()
+        del frig
+        res["roofline_factorized"] = f["roofline"] | {
+            "workload": "factorized_64k", "config": f["config"], "value": f["value"],
+            "unit": "tokens/s", "ms_per_step": f["ms_per_step"],
+            "ms_per_step_cold": f["ms_per_step_cold"], "step_hbm_frac": f["step_hbm_frac"],
+            "router": f["router"]} | ({"cpu_baseline": f["cpu_baseline"]} if "cpu_baseline" in f else {})
+        # the 4-layer fp32 toy step (parity-sized; latency only)
+        trig = DecodeRig(datagen.WORKLOADS["tiny_cla2"])
+        tpt = trig.point(1, trig.wl.ctx)
+        res["tiny_cla2"] = {"us_per_step": trig.warm_step_ms(tpt, 50, 10) * 1e3,
+                            "layers": trig.wl.n_layers, "batch": 1, "ctx": trig.wl.ctx,
+                            "dtype": "f32", "what": "append + decode of every layer, warm"}
+        trig.release()
+    calibration_copy()
+    print(json.dumps(res), flush=True)
+
+
+# ----------------------------------------------------------------------------
+# the batch x context grid
+# ----------------------------------------------------------------------------
+
+SWEEP = (("tinyllama_cla2", (1, 8, 16, 32, 64, 128), (512, 1024, 2048)),
+         ("cla2_64k", (1, 2, 4, 8), (16384, 32768, 65536)))
+
+
+def sweep_main(args):
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    points = []
+    for name, batches, ctxs in SWEEP:
+        base = datagen.WORKLOADS[name]
+        wl = base.with_(batch=max(batches), ctx=max(ctxs))
+        log(f"[sweep] setting up {name} at capacity B={wl.batch} ctx={wl.ctx}")
+        rig = DecodeRig(wl)
+        single = [l for l in range(wl.n_layers) if int(rig.src[l, 1]) < 0]
+        for ctx in ctxs:
+            for B in batches:
+                pt = rig.point(B, ctx)
+                ms = rig.warm_step_ms(pt, args.steps, args.warmup)
+                ms_cold = rig.cold_step_ms(pt, passes=1)
+                us, call_us, _ = rig.launches(pt, single, 1)
+                step_bytes = sum(rig.call_bytes(l, B, ctx) for l in range(wl.n_layers))
+                nbytes = rig.call_bytes(single[0], B, ctx)
+                p = {"workload": name, "batch": B, "ctx": ctx, "n_splits": pt["n_splits"],
+                     "tokens_s": B * 1000.0 / ms, "ms_per_step": ms,
+                     "step_gbs": step_bytes / (ms * 1e-3) / 1e9,
+                     "tokens_s_cold": B * 1000.0 / ms_cold, "ms_per_step_cold": ms_cold,
+                     "step_gbs_cold": step_bytes / (ms_cold * 1e-3) / 1e9,
+                     "kernel_us": us, "kernel_gbs": nbytes / (us * 1e-6) / 1e9,
+                     "call_us": call_us, "bytes_per_call": nbytes}
+                for k in ("step_gbs", "step_gbs_cold", "kernel_gbs"):
+                    p[k.replace("gbs", "frac")] = p[k] / HBM_PEAK_GBS
+                points.append(p)
+                log(f"[sweep] {name} B={B} ctx={ctx}: {p['tokens_s']:.0f} tok/s, kernel "
+                    f"{p['kernel_frac']:.1%} of HBM peak, cold step {p['step_frac_cold']:.1%}")
+                del pt
+        rig.release()
+        del rig
+    if args.sweep_out:
+        lines = ["| workload | batch | ctx | splits | tok/s (warm) | step GB/s (% peak) | "
+                 "tok/s (cold) | cold step GB/s (% peak) | kernel us | kernel GB/s (% peak) |",
+                 "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+        for p in points:
+            lines.append(f"| {p['workload']} | {p['batch']} | {p['ctx']} | {p['n_splits']} | "
+                         f"{p['tokens_s']:,.0f} | {p['step_gbs']:,.0f} ({p['step_frac']:.1%}) | "
+                         f"{p['tokens_s_cold']:,.0f} | {p['step_gbs_cold']:,.0f} "
+                         f"({p['step_frac_cold']:.1%}) | {p['kernel_us']:.1f} | "
+                         f"{p['kernel_gbs']:,.0f} ({p['kernel_frac']:.1%}) |")
+        open(args.sweep_out, "w").write("\n".join(lines) + "\n")
+    print(json.dumps({"metric": METRIC, "sweep": points}), flush=True)
 
 
 def main():
@@ -617,7 +1156,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="tinyllama_cla2",
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=["tiny_cla2", "tinyllama_cla2", "depthgraft", "cla2_64k",
                              "factorized_64k", "tinyllama_cla2_top", *PREFILL_WORKLOADS,
                              ENCODE_WORKLOAD])
@@ -625,6 +1164,10 @@ def main():
     ap.add_argument("--roofline-only", action="store_true",
                     help="only the cache-flushed per-launch timing loop (for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="default workload only: skip the factorized and toy extras")
+    ap.add_argument("--sweep", action="store_true", help="time the batch x context grid")
+    ap.add_argument("--sweep-out", metavar="FILE", help="with --sweep: markdown table to FILE")
     ap.add_argument("--summarize", metavar="PROFILE_DIR",
                     help="print the counter summary of a rocprofv3 profile directory and exit")
     ap.add_argument("--kernel", default="decode_kernel",
@@ -643,193 +1186,15 @@ def main():
         if args.record:
             print(record_profile(args.summarize, args.kernel, args.workload, s))
         return
+    if args.sweep:
+        return sweep_main(args)
     if args.workload == ENCODE_WORKLOAD:
         return encode_main(args)
     if args.workload in PREFILL_WORKLOADS:
         return prefill_main(args, args.workload)
     if args.prefill:
         return prefill_main(args, PREFILL_WORKLOAD)
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the path is a "
-              "single-GPU kernel library; sharding across GPUs is described, not built.",
-              file=sys.stderr)
-        sys.exit(2)
-
-    wl = datagen.WORKLOADS[args.workload]
-    torch.cuda.set_device(0)
-    log(f"[bench] setting up {wl.name}")
-    fact = wl.kind == "factorized"
-    if fact:
-        src, w, plan, cache, owners, rank = setup_factorized(wl)
-    else:
-        src, w, plan, cache, owners = setup(wl)
-    L, B = wl.n_layers, wl.batch
-    qs = [datagen.decode_q(wl, l, device="cuda") for l in range(L)]
-    # the step's token lands at position ctx-1 (rewritten every step); the
-    # query attends over ctx keys including it
-    pos = torch.full((B,), wl.ctx - 1, dtype=torch.int32, device="cuda")
-    if fact:
-        one = wl.with_(ctx=1)
-        r1 = rank[:, wl.ctx - 1:].contiguous()
-        new_f = {}
-        for l in range(L):
-            cc = datagen.pair_coeffs(one, 1000 + l, device="cuda") if l in owners else (None, None)
-            new_f[l] = cc + datagen.layer_residual(one, 1000 + l, r1, device="cuda")
-
-        def append(l):
-            ck, cv, dk, dv, sk, sv = new_f[l]
-            K.kvs_append_factorized(plan, cache, l, ck, cv, dk, dv, sk, sv, r1, pos,
-                                    stream=stream)
-        call_bytes = [fact_bytes_per_call(wl, rank)] * L
-    else:
-        new_kv = {l: datagen.owner_kv(wl, 1000 + l, device="cuda", ctx=1) for l in owners}
-
-        def append(l):
-            if l in new_kv:
-                K.kvs_append(plan, cache, l, new_kv[l][0], new_kv[l][1], pos, stream=stream)
-        call_bytes = [bytes_per_call(wl, src, l) for l in range(L)]
-    seq_len = torch.full((B,), wl.ctx, dtype=torch.int32, device="cuda")
-    n_splits = K.kvs_decode_splits(plan, B, wl.ctx)
-    ws = torch.zeros(K.kvs_decode_workspace_size(plan, B, n_splits), dtype=torch.uint8,
-                     device="cuda")
-    outs = [torch.empty((B, wl.n_q_heads, wl.head_dim), dtype=torch.float32, device="cuda")
-            for _ in range(L)]
-    stream = torch.cuda.current_stream()
-
-    def decode(l):
-        K.kvs_attn_decode(plan, cache, l, qs[l], seq_len, wl.ctx, out=outs[l],
-                          n_splits=n_splits, workspace=ws, stream=stream)
-
-    def step():
-        for l in range(L):
-            append(l)
-            decode(l)
-
-    res = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-           "warmup": args.warmup, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16" if wl.dtype == "bf16" else "f32",
-           "data": "synthetic", "config": describe(wl, src) | {"n_splits": n_splits}}
-
-    if not args.roofline_only:
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for _ in range(args.steps):
-            step()
-        t1.record(stream)
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / args.steps
-        step_bytes = sum(call_bytes)
-        res |= {"value": B * 1000.0 / ms, "ms_per_step": ms,
-                "step_hbm_gbs": step_bytes / (ms * 1e-3) / 1e9,
-                "step_hbm_frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-
-    # ---- per-launch roofline: cache flushed before every launch
-    flush = torch.ones((FLUSH_BYTES // 4 // 4096, 4096), dtype=torch.float32, device="cuda")
-    single = [l for l in range(L) if int(src[l, 1]) < 0]
-    mixed = [l for l in range(L) if int(src[l, 1]) >= 0]
-    timed = {}
-    for group in (single, mixed):
-        for l in group[:1]:
-            decode(l)                                     # warm the launch path
-        for _ in range(args.roofline_passes):
-            for l in group:
-                flush.sum(dim=0)
-                e0, e1, k0, k1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
-                K.kvs_time_next_launch(k0, k1, stream)
-                e0.record(stream)
-                decode(l)
-                e1.record(stream)
-                timed.setdefault(l, []).append((e0, e1, k0, k1))
-    torch.cuda.synchronize()
-
-    def avg_us(layers, kernel_only=True):
-        d = [(k0.elapsed_time(k1) if kernel_only else e0.elapsed_time(e1)) * 1e3
-             for l in layers for (e0, e1, k0, k1) in timed[l]]
-        return sum(d) / len(d)
-
-    dom = single if single else mixed
-    us = avg_us(dom)
-    nbytes = call_bytes[dom[0]]
-    achieved = nbytes / (us * 1e-6) / 1e9
-    res["roofline"] = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                       "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                       "kernel": ("fact_decode_kernel (factorized cache, split-K partitions)"
-                                  if fact else
-                                  decode_kernel_name(wl, not single) + ", "
-                                  + ("single-source layer" if single else "two-source layer")),
-                       "bytes_per_launch": nbytes, "avg_launch_us": us,
-                       "timing": "HIP events on the kernel's own start and end (hipExtLaunchKernel)",
-                       "avg_call_us": avg_us(dom, kernel_only=False),
-                       "launches": sum(len(timed[l]) for l in dom), "cache": "flushed"}
-    if single and mixed:
-        us2 = avg_us(mixed)
-        b2 = call_bytes[mixed[0]]
-        res["roofline_two_source"] = {"achieved": b2 / (us2 * 1e-6) / 1e9,
-                                      "frac": b2 / (us2 * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                                      "bytes_per_launch": b2, "avg_launch_us": us2,
-                                      "avg_call_us": avg_us(mixed, kernel_only=False)}
-    if fact:
-        # router statistics: the same cache-flushed launches with the entropy
-        # and peak side output, then the rank choice over every layer's
-        # statistics
-        stats = torch.empty((L, B, wl.n_q_heads, 2), dtype=torch.float32, device="cuda")
-        ev_s = []
-        for _ in range(args.roofline_passes):
-            for l in dom:
-                flush.sum(dim=0)
-                e0, e1, k0, k1 = (torch.cuda.Event(enable_timing=True) for _ in range(4))
-                K.kvs_time_next_launch(k0, k1, stream)
-                e0.record(stream)
-                K.kvs_attn_decode_stats(plan, cache, l, qs[l], seq_len, wl.ctx, out=outs[l],
-                                        stats=stats[l], n_splits=n_splits, workspace=ws,
-                                        stream=stream)
-                e1.record(stream)
-                ev_s.append((e0, e1, k0, k1))
-        router = K.kvs_router(0.5, 0.8, 0.5, wl.resid_rank_max, wl.resid_rank_max // 2, 0)
-        ranks = torch.empty(B, dtype=torch.uint8, device="cuda")
-        K.kvs_route_ranks(plan, stats, seq_len, router, rank_out=ranks, stream=stream)
-        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        r0.record(stream)
-        for _ in range(10):
-            K.kvs_route_ranks(plan, stats, seq_len, router, rank_out=ranks, stream=stream)
-        r1.record(stream)
-        torch.cuda.synchronize()
-        us_s = sum(k0.elapsed_time(k1) for e0, e1, k0, k1 in ev_s) * 1e3 / len(ev_s)
-        call_s = sum(e0.elapsed_time(e1) for e0, e1, k0, k1 in ev_s) * 1e3 / len(ev_s)
-        call = res["roofline"]["avg_call_us"]
-        res["router"] = {"decode_with_stats_us": us_s, "decode_us": us,
-                         "stats_overhead_frac": us_s / us - 1.0,
-                         "call_with_stats_us": call_s, "call_us": call,
-                         "stats_overhead_call_frac": call_s / call - 1.0,
-                         "route_us": r0.elapsed_time(r1) * 1e3 / 10,
-                         "route_sets": L, "routed_ranks": ranks.cpu().tolist()}
-    del flush
-    calibration_copy()
-    traffic = recorded_traffic(wl.name)
-    if traffic is not None:
-        res["roofline"]["traffic"] = traffic["bytes_per_launch"]
-        res["roofline"]["traffic_source"] = traffic["source"]
-
-    if not args.roofline_only and not args.no_cpu_baseline and not fact:
-        log("[bench] cpu baseline")
-        full = {}
-        for l in owners:
-            k, v = datagen.owner_kv(wl, l, device="cuda")
-            k[:, wl.ctx - 1:] = new_kv[l][0]
-            v[:, wl.ctx - 1:] = new_kv[l][1]
-            full[l] = (k, v)
-
-        def host_seq(b):
-            kk = {l: full[l][0][b:b + 1].cpu() for l in owners}
-            vv = {l: full[l][1][b:b + 1].cpu() for l in owners}
-            return kk, vv, [q[b:b + 1].cpu() for q in qs]
-
-        res["cpu_baseline"] = cpu_baseline(wl, src, w, host_seq)
-    print(json.dumps(res), flush=True)
+    return decode_main(args)
 
 
 if __name__ == "__main__":

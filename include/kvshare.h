@@ -211,7 +211,11 @@ KVS_API kvs_status kvs_decode_workspace_size(const kvs_plan* plan, int32_t batch
 
 /* ----------------------------------------------------------------- writing */
 
-/* Write n new tokens' K/V of an owner layer into its slot.
+/* Write n new tokens' K/V of an owner layer into its slot.  Only layers that
+ * compute their own K/V store them; the layers that reuse them store nothing
+ * ("Reducing Transformer Key-Value Cache Size with Cross-Layer Attention",
+ * Methodology: some layers compute fresh K/V, the layers after them reuse
+ * those; Abstract: the cache holds the owners' entries only).
  *   k, v       device [batch][n][Hkv][hd], cache dtype
  *   start_pos  device int32 [batch]: token i of sequence b goes to position
  *              start_pos[b] + i.  Positions outside [0, max_ctx), or whose
@@ -222,7 +226,11 @@ KVS_API kvs_status kvs_append(const kvs_plan* plan, const kvs_cache* cache, int3
                               const void* k, const void* v, int32_t n,
                               const int32_t* start_pos, int32_t batch, void* stream);
 
-/* Factorized write of n tokens for `layer`.
+/* Factorized write of n tokens for `layer`: the entries of the factorized
+ * cache of "DepthWeave-KV: Smarter KV Cache Compression by Sharing Across
+ * Layers and Adapting Per Token" (Core Mechanism: coefficients on a basis
+ * shared by a layer pair, and a per-layer low-rank residual kept as int8
+ * codes; Framework Shift: the residual's rank is chosen per token).
  *   ck, cv     device bf16 [batch][n][Hkv][R]: the pair coefficients; given
  *              only by the layer that owns the pair's slot (else NULL)
  *   dk, dv     device int8 [batch][n][Hkv][Rmax]; codes at j >= r_t are
@@ -344,7 +352,16 @@ KVS_API kvs_status kvs_residual_bases(const kvs_plan* plan, int32_t n_items, con
 
 /* One decode query per (sequence, q head) of `layer` over keys
  * 0..seq_len[b]-1 of the layer's source(s) (the current token's entry
- * included: its owner appends it first).
+ * included: its owner appends it first).  The layer attends over the cached
+ * K/V of its source layer ("Reducing Transformer Key-Value Cache Size with
+ * Cross-Layer Attention", Methodology), of the stride-aligned source pair
+ * mixed with the layer's weights ("DepthGraft: Structural Regularization
+ * through Hierarchical Cross-Layer KV Reconstruction", Abstract), or of the
+ * factorized entries read in place ("DepthWeave-KV: Smarter KV Cache
+ * Compression by Sharing Across Layers and Adapting Per Token", Core
+ * Mechanism: basis lookup, residual dequantization and attention in one
+ * pass).  Keys of a page whose page-table entry lies outside
+ * [0, n_phys_pages) get no weight (the entry is never dereferenced).
  *   q           device [batch][Hq][hd], cache dtype (bf16 for factorized)
  *   seq_len     device int32 [batch]; values are clamped to [0, max_ctx]; a
  *               sequence with no keys yields zeros
@@ -362,12 +379,19 @@ KVS_API kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cache,
 /* A chunk of n queries per sequence that sit at the last n positions of each
  * sequence (their K/V already appended): query i of sequence b is at
  * P = seq_len[b] - n + i and sees keys 0..P when causal != 0 (inclusive
- * diagonal), else keys 0..seq_len[b]-1.  Query and key tiles go through bf16
+ * diagonal), else keys 0..seq_len[b]-1.  The source layers' caches serve the
+ * prompt's keys as they serve the decode ("Reducing Transformer Key-Value
+ * Cache Size with Cross-Layer Attention", Methodology); only the owner
+ * layers of a DepthGraft map need the whole prompt ("DepthGraft: Structural
+ * Regularization through Hierarchical Cross-Layer KV Reconstruction",
+ * Abstract: prefill completes early).  Keys of a page whose page-table entry
+ * lies outside [0, n_phys_pages) get no weight, as in the decode.  Query and key tiles go through bf16
  * MFMA with fp32 accumulation; a two-source layer's mixed K~/V~ tiles (mixed
  * in fp32) enter the MFMA as their bf16 rounding plus the bf16 rounding of
  * the remainder.
  *   q        device bf16 [batch][n][Hq][hd]
- *   seq_len  device int32 [batch], each >= n
+ *   seq_len  device int32 [batch], each >= n; a row whose position P is
+ *            below 0 (seq_len[b] < n) sees no key and yields zeros
  *   out      device [batch][n][Hq][hd] of out_dtype
  * Dense bf16 plans, and factorized plans (head_dim 64/128, ranks 32/16),
  * which attend in the coefficient space: q~ = B^K q and u~ = U^K q once per

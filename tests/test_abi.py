@@ -208,4 +208,8 @@ def test_compute_calls_validate_before_launch():
     assert _raw_decode(plan, c, 1, a + 4, a, 1, 128, 2, a, 0, a, ws) == K.KVS_ERR_ALIGN
     assert _raw_decode(plan, c, 1, a, a, 1, 128, 5000, a, 0, a, 1 << 40) == K.KVS_ERR_RANGE
     assert _raw_decode(plan, c, 1, a, None, 1, 128, 2, a, 0, a, ws) == K.KVS_ERR_ARG
-    assert "workspace" in K.lib().kvs_last_error().decode() or True
+    assert "null" in K.lib().kvs_last_error().decode()
+    # the last error names the failed check of the call that set it
+    assert _raw_decode(plan, c, 1, a, a, 1, 128, 2, a, 0, a, ws - 4) == K.KVS_ERR_RANGE
+    msg = K.lib().kvs_last_error().decode()
+    assert "workspace too small" in msg and str(ws) in msg

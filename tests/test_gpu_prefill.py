@@ -36,6 +36,10 @@ CASES = {
     "depthgraft_g1_hd128_few_keys": (W["cla2_64k"].with_(n_layers=6, n_q_heads=1, n_kv_heads=1, share="depthgraft",
                                                          dg_stride=2), 2, 100, [97, 100], 77, True),
     "g32_hd64": (W["tinyllama_cla2"].with_(n_layers=2, n_q_heads=32, n_kv_heads=1), 2, 140, [140, 75], 75, True),
+    # the DepthGraft shape (32 q / 8 KV heads, hd 128, owner and mixed layers)
+    # at its decode batch of 8, context reduced, ragged lengths
+    "depthgraft_b8": (W["depthgraft"].with_(n_layers=6, dg_stride=2), 8, 384,
+                      [384, 300, 257, 384, 200, 129, 350, 321], 128, True),
 }
 
 
