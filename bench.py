@@ -1080,7 +1080,7 @@ def decode_main(args):
         del frig
         res["roofline_factorized"] = f["roofline"] | {
             "workload": "factorized_64k", "config": f["config"], "value": f["value"],
-            "unit": "tokens/s", "ms_per_step": f["ms_per_step"],
+            "value_unit": "tokens/s", "ms_per_step": f["ms_per_step"],
             "ms_per_step_cold": f["ms_per_step_cold"], "step_hbm_frac": f["step_hbm_frac"],
             "router": f["router"]} | ({"cpu_baseline": f["cpu_baseline"]} if "cpu_baseline" in f else {})
         # the 4-layer fp32 toy step (parity-sized; latency only)
