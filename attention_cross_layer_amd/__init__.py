@@ -35,7 +35,7 @@ EXPORTS = ("kvs_share_plan", "kvs_plan_free", "kvs_plan_layer", "kvs_plan_summar
            "kvs_append_factorized", "kvs_encode_workspace_size", "kvs_encode_factorized",
            "kvs_basis_workspace_size", "kvs_pair_basis", "kvs_pair_bases", "kvs_residual_basis",
            "kvs_residual_bases",
-           "kvs_attn_decode", "kvs_attn_decode_stats", "kvs_route_ranks",
+           "kvs_attn_decode", "kvs_attn_decode_noalloc", "kvs_attn_decode_stats", "kvs_route_ranks",
            "kvs_attn_prefill_chunk", "kvs_time_next_launch", "kvs_last_error")
 
 
@@ -123,6 +123,8 @@ def lib():
                                         vp, i32, vp]),
         "kvs_attn_decode": (i32, [vp, P(kvs_cache), i32, vp, vp, i32, i32, i32, vp, i32, vp, sz,
                                   vp]),
+        "kvs_attn_decode_noalloc": (i32, [vp, P(kvs_cache), i32, vp, vp, i32, i32, i32, vp, i32,
+                                          vp]),
         "kvs_attn_prefill_chunk": (i32, [vp, P(kvs_cache), i32, vp, i32, vp, i32, i32, vp, i32,
                                          vp]),
         "kvs_encode_workspace_size": (i32, [vp, i32, i32, P(sz)]),
@@ -430,6 +432,17 @@ def kvs_attn_decode(plan: Plan, cache: Cache, layer: int, q: torch.Tensor,
                                  _ptr(seq_len), B, max_seq_len, n_splits, _ptr(out),
                                  _dtype_code(out.dtype), _ptr(workspace), workspace.numel(),
                                  _stream(stream)))
+    return out
+
+
+def kvs_attn_decode_noalloc(plan: Plan, cache: Cache, layer: int, q: torch.Tensor,
+                            seq_len: torch.Tensor, max_seq_len: int, out: torch.Tensor,
+                            n_splits: int = 0, stream=None) -> torch.Tensor:
+    """kvs_attn_decode with the partials in the library's device scratch:
+    the caller passes the output buffer; nothing is allocated."""
+    _check(lib().kvs_attn_decode_noalloc(plan.handle, ctypes.byref(cache.struct), layer, _ptr(q),
+                                         _ptr(seq_len), q.shape[0], max_seq_len, n_splits,
+                                         _ptr(out), _dtype_code(out.dtype), _stream(stream)))
     return out
 
 

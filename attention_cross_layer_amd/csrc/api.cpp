@@ -192,6 +192,36 @@ extern "C" kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cac
                      nullptr, workspace, ws_bytes, stream);
 }
 
+extern "C" kvs_status kvs_attn_decode_noalloc(const kvs_plan* plan, const kvs_cache* cache,
+                                              int32_t layer, const void* q, const int32_t* seq_len,
+                                              int32_t batch, int32_t max_seq_len, int32_t n_splits,
+                                              void* out, int32_t out_dtype, void* stream) {
+  clear_error();
+  kvs_status st = check_layer(plan, layer);
+  if (st != KVS_OK) return st;
+  if ((st = check_batch(plan, batch)) != KVS_OK) return st;
+  const size_t cap = scratch_bytes();
+  size_t need = 0;
+  if (n_splits == 0) {
+    // the library's choice, lowered until the partials fit the scratch
+    if ((st = kvs_decode_splits(plan, batch, max_seq_len, &n_splits)) != KVS_OK) return st;
+    if ((st = kvs_decode_workspace_size(plan, batch, 1, &need)) != KVS_OK) return st;
+    const size_t fit = need ? cap / need : size_t(n_splits);
+    if (fit >= 1 && size_t(n_splits) > fit) n_splits = int32_t(fit);
+  }
+  if ((st = kvs_decode_workspace_size(plan, batch, n_splits, &need)) != KVS_OK) return st;
+  if (need > cap)
+    return fail(KVS_ERR_RANGE, "kvs_attn_decode_noalloc: batch " + std::to_string(batch) + " x " +
+                                   std::to_string(n_splits) + " partitions need " +
+                                   std::to_string(need) + " bytes of partials; the library's "
+                                   "scratch holds " + std::to_string(cap) +
+                                   " (use fewer partitions or kvs_attn_decode with a workspace)");
+  void* ptr = nullptr;
+  if ((st = hip_status(scratch_address(&ptr), "scratch address")) != KVS_OK) return st;
+  return decode_impl(plan, cache, layer, q, seq_len, batch, max_seq_len, n_splits, out, out_dtype,
+                     nullptr, ptr, cap, stream);
+}
+
 extern "C" kvs_status kvs_attn_decode_stats(const kvs_plan* plan, const kvs_cache* cache,
                                             int32_t layer, const void* q, const int32_t* seq_len,
                                             int32_t batch, int32_t max_seq_len, int32_t n_splits,

@@ -278,6 +278,12 @@ int launch_route(const RouteLaunch& a, void* stream);
 
 const char* hip_error_name(int err);
 
+// Device scratch of kvs_attn_decode_noalloc: its size, and this device's
+// address of it (taken once per device with hipGetSymbolAddress); returns a
+// hipError_t value.
+size_t scratch_bytes();
+int scratch_address(void** out);
+
 }  // namespace kvs
 
 struct kvs_plan {

@@ -376,6 +376,27 @@ KVS_API kvs_status kvs_attn_decode(const kvs_plan* plan, const kvs_cache* cache,
                                    void* out, int32_t out_dtype, void* workspace,
                                    size_t ws_bytes, void* stream);
 
+/* kvs_attn_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and results as kvs_attn_decode with the same
+ * n_splits, with the split-K partials held in a 16 MiB device array that the
+ * library keeps (one per GPU, alive until the process ends) instead of a
+ * caller workspace.  The call allocates nothing itself; the first call on a
+ * device looks the array's address up (hipGetSymbolAddress) with that device
+ * current.
+ *   n_splits  0: the library's choice, lowered until the partials fit; a
+ *             given count whose partials (kvs_decode_workspace_size) exceed
+ *             16 MiB -> KVS_ERR_RANGE, nothing launched
+ * Every partition writes its whole partial row before the merge reads it, so
+ * nothing in the array needs clearing between calls.  All calls on one GPU
+ * share the array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.  Other arguments
+ * and errors as kvs_attn_decode. */
+KVS_API kvs_status kvs_attn_decode_noalloc(const kvs_plan* plan, const kvs_cache* cache,
+                                           int32_t layer, const void* q, const int32_t* seq_len,
+                                           int32_t batch, int32_t max_seq_len, int32_t n_splits,
+                                           void* out, int32_t out_dtype, void* stream);
+
 /* A chunk of n queries per sequence that sit at the last n positions of each
  * sequence (their K/V already appended): query i of sequence b is at
  * P = seq_len[b] - n + i and sees keys 0..P when causal != 0 (inclusive
