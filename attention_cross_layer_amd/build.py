@@ -25,6 +25,12 @@ HIPFLAGS = ["-O3", "-fPIC", "-fvisibility=hidden", "-std=c++17", f"--offload-arc
             # packed fp32 VALU forms are kept out of the generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", INCLUDE, "-I", CSRC, "-Wno-unused-command-line-argument"]
+# Per-file additions.  The factorized decode rescales and reads its MFMA
+# accumulators with VALU instructions, which cannot take AGPR operands: in
+# the AGPR form the compiler copied all 48 value accumulators into AGPRs and
+# back on every page (about 165 v_accvgpr moves per page); in the VGPR form
+# none (32.5 vs 33.4 us per 64K-context layer call, one box).
+FILE_FLAGS = {"k_factorized.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():
@@ -53,7 +59,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         objs.append(o)
     for f in hip:
         o = os.path.join(BUILD, f + ".o")
-        cmds.append([HIPCC] + HIPFLAGS + ["-c", os.path.join(CSRC, f), "-o", o])
+        cmds.append([HIPCC] + HIPFLAGS + FILE_FLAGS.get(f, []) + ["-c", os.path.join(CSRC, f), "-o", o])
         objs.append(o)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))

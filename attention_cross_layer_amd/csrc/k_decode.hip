@@ -170,7 +170,7 @@ __device__ __forceinline__ void load_k(uint4 (&kr)[NSRC][HD / Traits<T>::E], con
   for (int s = 0; s < NSRC; ++s)
 #pragma unroll
     for (int c = 0; c < HD / E; ++c)
-      kr[s][c] = *reinterpret_cast<const uint4*>(kt[s] + c * (kPage * E) + lane * E);
+      kr[s][c] = dev::ld16_stream(kt[s] + c * (kPage * E) + lane * E);
 }
 
 template <typename T, int HD, int NSRC, int PPL, int NPH, int DPL>
@@ -180,7 +180,7 @@ __device__ __forceinline__ void load_v(uint4 (&vr)[NSRC][PPL], const T* const (&
   for (int s = 0; s < NSRC; ++s)
 #pragma unroll
     for (int j = 0; j < PPL; ++j)
-      vr[s][j] = *reinterpret_cast<const uint4*>(vt[s] + (ph + NPH * j) * (HD * 2) + quad * (DPL * 2));
+      vr[s][j] = dev::ld16_stream(vt[s] + (ph + NPH * j) * (HD * 2) + quad * (DPL * 2));
 }
 
 template <typename T, int HD, int G, int NSRC>

@@ -145,15 +145,15 @@ __device__ __forceinline__ uint32_t quad_transpose(uint32_t x, uint32_t sel1, ui
 // Max over the 16 quads of a wave for each lane position p (the lanes l with
 // l % 4 == p), returned to every such lane.
 __device__ __forceinline__ float quad_column_max(float x) {
-  x = fmaxf(x, dev::dpp<0x124>(x));   // row_ror:4
-  x = fmaxf(x, dev::dpp<0x128>(x));   // row_ror:8: every lane holds its row's max
+  x = dev::fmax_ieee(x, dev::dpp<0x124>(x));   // row_ror:4
+  x = dev::fmax_ieee(x, dev::dpp<0x128>(x));   // row_ror:8: every lane holds its row's max
   // across the two halves, then across row pairs (v_permlane32_swap /
   // v_permlane16_swap with both operands x: the two results hold the two
   // partners' values)
   const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  x = dev::fmax_ieee(__uint_as_float(h[0]), __uint_as_float(h[1]));
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return dev::fmax_ieee(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Sum over the 4 quads of each 16-lane row for each lane position p: lane
@@ -167,6 +167,8 @@ __device__ __forceinline__ float quad_row_sum(float x) {
 using dev::kOOB;
 using dev::ld16;
 using dev::ld8;
+using dev::ld2;
+using dev::kStream;
 using dev::rsrc;
 
 // One page as loaded: cK, codes and meta with lane = token; cV with lane =
@@ -268,19 +270,18 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
   // rank | granule offset << 8 of this lane's token; 0 when there is none
   auto load_meta = [&](int pg, int ph) -> uint32_t {
     const bool on = ph >= 0 && lane < n_keys - pg * kPage;
-    return __builtin_amdgcn_raw_buffer_load_b16(r_meta, (int)(on ? (uint32_t)(ph * kPage + lane) * 2 : kOOB),
-                                                0, 0);
+    return ld2<kStream>(r_meta, on ? (uint32_t)(ph * kPage + lane) * 2 : kOOB);
   };
   auto load_coefs = [&](int ph, PageRegs& r) {
     const uint32_t page_kv = (uint32_t)ph * H + kvh;
     const uint32_t cb = ph >= 0 ? page_kv * (kPage * kR * 2) : kOOB;
     const uint32_t sb = ph >= 0 ? page_kv * (kPage * 2) : kOOB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.ck[i] = ld16(r_ck, cb + (i * 64 + lane) * 16);
+    for (int i = 0; i < 4; ++i) r.ck[i] = ld16<kStream>(r_ck, cb + (i * 64 + lane) * 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.cv[i] = ld16(r_cv, cb + (i * 64 + lane) * 16);
-    r.sk = ld8(r_sk, sb + quad * 8);
-    r.sv = ld8(r_sv, sb + quad * 8);
+    for (int i = 0; i < 4; ++i) r.cv[i] = ld16<kStream>(r_cv, cb + (i * 64 + lane) * 16);
+    r.sk = ld8<kStream>(r_sk, sb + quad * 8);
+    r.sv = ld8<kStream>(r_sv, sb + quad * 8);
   };
   auto load_codes = [&](int ph, uint32_t meta, PageRegs& r) {
     const int rank = min((int)(meta & 0xffu), kRM);
@@ -289,10 +290,10 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
     // meta != 0 only for pages with ph >= 0
     const uint32_t blob = ((uint32_t)ph * H + kvh) * (kGranules * 8) + g0 * 8;
     const uint32_t o0 = ng >= 1 ? blob : kOOB, o1 = ng == 2 ? blob + 8 : kOOB;
-    r.dk[0] = ld8(r_dk, o0);
-    r.dk[1] = ld8(r_dk, o1);
-    r.dv[0] = ld8(r_dv, o0);
-    r.dv[1] = ld8(r_dv, o1);
+    r.dk[0] = ld8<kStream>(r_dk, o0);
+    r.dk[1] = ld8<kStream>(r_dk, o1);
+    r.dv[0] = ld8<kStream>(r_dv, o0);
+    r.dv[1] = ld8<kStream>(r_dv, o1);
   };
 
   // ---- absorbed query: qt[h][i] = (row i of B^K, or U^K for i >= R) . q_h.
@@ -470,11 +471,12 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
         z[e] = (ok[e] && head_ok) ? v : -INFINITY;
       }
       // ---- online softmax with one running max per head (uniform over the wave)
-      const float mt = quad_column_max(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-      const float mn = fmaxf(m_run[hb], mt);
+      const float mt = quad_column_max(dev::fmax_ieee(dev::fmax3_ieee(z[0], z[1], z[2]), z[3]));
+      const bool bump = mt > m_run[hb];
+      const float mn = bump ? mt : m_run[hb];
       const float mu = mn == -INFINITY ? 0.f : mn;
       // 1 exactly while the max holds (also for heads past G, whose max stays -inf)
-      const float alpha = m_run[hb] == mn ? 1.f : dev::fast_exp2(m_run[hb] - mu);
+      const float alpha = bump ? dev::fast_exp2(m_run[hb] - mu) : 1.f;
       const float m_old = m_run[hb];
       m_run[hb] = mn;
       if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
