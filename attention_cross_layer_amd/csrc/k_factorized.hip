@@ -119,6 +119,13 @@ __device__ __forceinline__ f4_t mfma4(uint32_t a0, uint32_t a1, uint32_t b0, uin
                                                 __builtin_bit_cast(s4_t, b), c, 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+
+__device__ __forceinline__ f4_t mfma16(const uint4& a, const uint4& b, f4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const bf2_t v = {(__bf16)lo, (__bf16)hi};
@@ -296,22 +303,27 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
     r.dv[1] = ld8<kStream>(r_dv, o1);
   };
 
-  // ---- absorbed query: qt[h][i] = (row i of B^K, or U^K for i >= R) . q_h.
-  // The operands of a thread's first element are requested before the first
-  // page, so that waiting for them does not wait for the page as well.
-  constexpr int NE = NB * 4 * kW;
-  const int e0h = tid / kW, e0i = tid % kW;
-  const bool live0 = tid < NE && e0h < G;
-  uint4 x0[HD / 8], y0[HD / 8];
-  {
-    // threads without an element read row e0i of head 0's operands, unused
-    const uint16_t* row = e0i < kR ? a.bk + ((size_t)kvh * kR + e0i) * HD
-                                   : a.uk + ((size_t)kvh * kRM + (e0i - kR)) * HD;
-    const uint16_t* qr = a.q + ((size_t)b * a.n_q_heads + (size_t)kvh * G + (live0 ? e0h : 0)) * HD;
+  // ---- absorbed query: qt[h][i] = (row i of [B^K; U^K]) . q_h for the 48
+  // rows i and the G <= 8 heads h, on v_mfma_f32_16x16x32_bf16: waves 0..2
+  // take one 16-row block each (A = 16 rows x 32 dims, B = 32 dims x 16
+  // heads, the columns past G zero), HD/32 steps.  Products of bf16 values
+  // are exact and summed in fp32.  Each lane requests its two 16-byte
+  // operands per step before the first page, so the contraction waits only
+  // for them; a workgroup reads the 12 KB of bases and its queries once.
+  constexpr int KSQ = HD / 32;
+  uint4 qa[KSQ], qb[KSQ];
+  const int qh = lane & 15;              // head column of this lane
+  const int qk = 8 * (lane >> 4);        // its first dim within each 32-dim step
+  if (wave < 3) {
+    const int r = 16 * wave + qh;        // row of [B^K; U^K]
+    const uint16_t* row = r < kR ? a.bk + ((size_t)kvh * kR + r) * HD
+                                 : a.uk + ((size_t)kvh * kRM + (r - kR)) * HD;
+    const uint16_t* qr = a.q + ((size_t)b * a.n_q_heads + (size_t)kvh * G + min(qh, G - 1)) * HD;
 #pragma unroll
-    for (int c = 0; c < HD / 8; ++c) {
-      x0[c] = *reinterpret_cast<const uint4*>(row + c * 8);
-      y0[c] = *reinterpret_cast<const uint4*>(qr + c * 8);
+    for (int ks = 0; ks < KSQ; ++ks) {
+      qa[ks] = *reinterpret_cast<const uint4*>(row + 32 * ks + qk);
+      const uint4 y = *reinterpret_cast<const uint4*>(qr + 32 * ks + qk);
+      qb[ks] = qh < G ? y : make_uint4(0, 0, 0, 0);
     }
   }
 
@@ -324,38 +336,15 @@ __global__ __launch_bounds__(256) void fact_decode_kernel(FactParams a) {
   uint32_t meta_b = load_meta(pg0 + 4, ph_b);
   load_coefs(ph0, bufA);
 
-  if (tid < NE) {
-    float acc = 0.f;
-    if (live0) {
+  if (wave < 3) {
+    f4_t d = f4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < HD / 8; ++c) {
-        acc = dot2_bf16(x0[c].x, y0[c].x, acc);
-        acc = dot2_bf16(x0[c].y, y0[c].y, acc);
-        acc = dot2_bf16(x0[c].z, y0[c].z, acc);
-        acc = dot2_bf16(x0[c].w, y0[c].w, acc);
-      }
-    }
-    qt[e0h][e0i] = acc * a.scale_log2;
-  }
-  // further elements (more than 256 when G > 4)
-  for (int e = tid + 256; e < NE; e += 256) {
-    const int h = e / kW, i = e % kW;
-    float acc = 0.f;
-    if (h < G) {
-      const uint16_t* row = i < kR ? a.bk + ((size_t)kvh * kR + i) * HD
-                                   : a.uk + ((size_t)kvh * kRM + (i - kR)) * HD;
-      const uint16_t* qr = a.q + ((size_t)b * a.n_q_heads + (size_t)kvh * G + h) * HD;
+    for (int ks = 0; ks < KSQ; ++ks) d = mfma16(qa[ks], qb[ks], d);
+    // lane: head qh, rows 16 * wave + 4 * (lane / 16) + j
+    if (qh < NB * 4) {
 #pragma unroll
-      for (int c = 0; c < HD / 8; ++c) {
-        const uint4 x = *reinterpret_cast<const uint4*>(row + c * 8);
-        const uint4 y = *reinterpret_cast<const uint4*>(qr + c * 8);
-        acc = dot2_bf16(x.x, y.x, acc);
-        acc = dot2_bf16(x.y, y.y, acc);
-        acc = dot2_bf16(x.z, y.z, acc);
-        acc = dot2_bf16(x.w, y.w, acc);
-      }
+      for (int j = 0; j < 4; ++j) qt[qh][16 * wave + 4 * (lane >> 4) + j] = d[j] * a.scale_log2;
     }
-    qt[h][i] = acc * a.scale_log2;
   }
   load_codes(ph0, meta0, bufA);
   __syncthreads();
