@@ -441,7 +441,7 @@ def record_profile(prof_dir, kernel, workload, s):
     top = [r for r in allk if "kvs::" in r["Name"]] + [r for r in allk if "kvs::" not in r["Name"]][:4]
     alg = algorithmic_bytes(wl, kernel)
     fetch, write = s["FETCH_SIZE"]["bytes_per_dispatch"], s["WRITE_SIZE"]["bytes_per_dispatch"]
-    cmd = (f"python3 bench.py --workload {workload} --steps 8 --warmup 2" if prefill
+    cmd = (f"python3 bench.py --workload {workload} --steps 8 --warmup 2 --no-cpu-baseline" if prefill
            else f"python3 bench.py --workload {workload} --roofline-only")
     lines = [
         f"# `{kernel}` on `{workload}`", "",
@@ -535,6 +535,37 @@ def prefill_wl(workload):
         return datagen.WORKLOADS["factorized_64k"].with_(batch=1, ctx=8192, prefill_n=4096,
                                                          prefill_batch=1)
     return datagen.WORKLOADS["depthgraft"].with_(batch=1)
+
+
+FP32_VECTOR_PEAK_TFLOPS = 157.3
+# VALU lane-operations an unmasked (query, key) pair needs in an online
+# softmax whose probabilities feed a bf16 product: one fma (scale and
+# shift), one exp2 (a transcendental: a quarter of the fma rate, so four fma
+# slots), and half of a max3, a pack to bf16 and a dot2 into the running sum
+# (each covers two pairs).
+VALU_SLOTS_PER_PAIR = 1 + 4 + 3 * 0.5
+
+
+def issue_roofline(wl, fact, us):
+    """The prefill chunk against what issuing its instructions allows: the
+    softmax's VALU work per pair at the fp32 vector rate plus the MFMA work
+    per pair as the kernel issues it, the two not overlapped (per-SIMD issue
+    counters show them serialised).  MFMA FLOPs issued per pair: dense
+    4*hd (two products); factorized 2*(2*R + 2*Rmax) for the scores (q~, u~
+    as bf16 high and low parts) + 2*(R + 2*Rmax) for the values (the
+    residual product runs 32 rows wide, half of them zero)."""
+    n, T = wl.prefill_n, wl.ctx
+    pairs = wl.n_q_heads * (n * (T - n) + n * (n + 1) // 2)
+    R, Rm = wl.basis_rank, wl.resid_rank_max
+    mfma_flops = (2 * (2 * R + 2 * Rm) + 2 * (R + 2 * Rm)) if fact else 4 * wl.head_dim
+    valu_s = VALU_SLOTS_PER_PAIR / (FP32_VECTOR_PEAK_TFLOPS * 1e12 / 2)
+    mfma_s = mfma_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    peak = 1.0 / (valu_s + mfma_s)
+    achieved = pairs / (us * 1e-6)
+    return {"bound": "alu", "unit": "pairs/s", "achieved": achieved, "peak": peak,
+            "frac": achieved / peak, "valu_slots_per_pair": VALU_SLOTS_PER_PAIR,
+            "mfma_flops_per_pair_issued": mfma_flops,
+            "note": "softmax VALU at the fp32 vector rate + issued MFMA at the bf16 rate, serialised"}
 
 
 def prefill_kernel_flops(wl, kernel):
@@ -651,6 +682,7 @@ def prefill_main(args, workload):
         # the rate of an attention over rebuilt hd-wide rows doing the same job
         dense = prefill_flops(n, T, wl.n_q_heads, wl.head_dim)
         res["roofline"]["dense_equivalent_tflops"] = dense / (us * 1e-6) / 1e12
+    res["roofline_alu"] = issue_roofline(wl, fact, us)
     calibration_copy()
     traffic = recorded_traffic(workload)
     if traffic is not None:
