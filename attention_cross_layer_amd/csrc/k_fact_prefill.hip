@@ -72,7 +72,12 @@ constexpr int kBRow = 48 + 8;     // transposed basis row pitch in coefficients
 constexpr int kCK = 64 * kR;      // staged page parts, bf16 elements
 constexpr int kSK = 64 * kRM;
 constexpr int kCV = kR * kVRow;
-constexpr int kSV = kRM * kVRow;
+// S^V^T is staged with 32 rows: rows 0..15 the scaled value codes of each
+// page, row 16 ones and rows 17..31 zeros, written once per launch, so the
+// 32-row value product accumulates the softmax's running sum in its row 16
+// and needs no per-tile selects for the rows past the codes
+constexpr int kSV = 2 * kRM * kVRow;
+constexpr int kOnesRow = kRM;
 constexpr int kTile = kCK + kSK + kCV + kSV;
 
 struct FactPrefillParams {
@@ -111,7 +116,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
 constexpr float kBumpLog2 = 8.f;                // lazy-maximum slack (log2 units)
 
 // Position of entry j inside its 16-wide group with quads 1 and 2 swapped
@@ -255,7 +259,9 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
       const int ia = 8 * mh + i4;
       const int k0 = key0 + 4 * tq;
       uint32_t m0 = 0, m1 = 0;
-      if (page_ok) {
+      if (page_ok && key0 + 64 <= T) {          // uniform: a page wholly in range
+        m0 = m1 = 0xffffffffu;
+      } else if (page_ok) {
         m0 = (k0 < T ? 0x0000ffffu : 0u) | (k0 + 1 < T ? 0xffff0000u : 0u);
         m1 = (k0 + 2 < T ? 0x0000ffffu : 0u) | (k0 + 3 < T ? 0xffff0000u : 0u);
       }
@@ -275,6 +281,14 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
       svt[(4 * cq + 3) * kVRow] = (uint16_t)(w.y >> 16);
     }
   };
+
+  // ---- the permanent rows of both S^V^T buffers (ones, zeros); ordered
+  // before their first read by the loop's first barrier
+  for (int e = tid; e < 2 * kRM * kVRow; e += 256) {
+    const int buf = e / (kRM * kVRow), r = (e / kVRow) % kRM;
+    lds[buf * kTile + kCK + kSK + kCV + (kRM + r) * kVRow + e % kVRow] =
+        r == 0 ? (uint16_t)0x3F80u : (uint16_t)0u;
+  }
 
   // ---- first page's requests, then the query contraction with the bases.
   // Physical pages are looked up a tile before the loads that need them.
@@ -310,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
   }
 
   f32x16_t acc_c = f32x16_t{}, acc_d = f32x16_t{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;
   const float bump_gap = kBumpLog2 / a.scale_log2;   // in raw score units
 
   for (int t = 0; t < n_tiles; ++t) {
@@ -375,7 +389,6 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
     const float neg = mn == -INFINITY ? 0.f : -mn * a.scale_log2;
     const float alpha = bump ? dev::fast_exp2(fmaf(m_run, a.scale_log2, neg)) : 1.f;
     m_run = mn;
-    float lt = 0.f;
     uint4 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -389,13 +402,8 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
         w.y = pack_bf16(p[2], p[3]);
         w.z = pack_bf16(p[4], p[5]);
         w.w = pack_bf16(p[6], p[7]);
-        lt = dev::dot2_bf16(w.x, kOnesBf16x2, lt);
-        lt = dev::dot2_bf16(w.y, kOnesBf16x2, lt);
-        lt = dev::dot2_bf16(w.z, kOnesBf16x2, lt);
-        lt = dev::dot2_bf16(w.w, kOnesBf16x2, lt);
         pb[2 * kb + sh] = w;
       }
-    l_run = fmaf(l_run, alpha, lt);
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -407,12 +415,11 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
     // ---- A^T += C^V^T P^T, D^T += S^V^T P^T; step sp covers keys
     // 16sp + 8(e/4) + 4hh + e%4, stored at positions 16sp + 8hh + e
     const uint16_t* cvt = base + kCK + kSK + col * kVRow + 8 * hh;
-    const uint16_t* svt = base + kCK + kSK + kCV + (col & 15) * kVRow + 8 * hh;
+    const uint16_t* svt = base + kCK + kSK + kCV + col * kVRow + 8 * hh;
 #pragma unroll
     for (int sp = 0; sp < 4; ++sp) {
       const uint4 av = *reinterpret_cast<const uint4*>(cvt + 16 * sp);
-      uint4 ad = *reinterpret_cast<const uint4*>(svt + 16 * sp);
-      if (col >= kRM) ad = make_uint4(0, 0, 0, 0);
+      const uint4 ad = *reinterpret_cast<const uint4*>(svt + 16 * sp);
       acc_c = mfma32(av, pb[sp], acc_c);
       acc_d = mfma32(ad, pb[sp], acc_d);
     }
@@ -445,7 +452,9 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
   split8(acc_c, 8, chi[1], clo[1]);
   split8(acc_d, 0, dhi, dlo);
 
-  const float l_row = l_run + __shfl_xor(l_run, 32);
+  // the running sum: row 16 of D^T (register 8 of lanes 0..31; lanes
+  // 32..63 hold row 20 there, a zero row)
+  const float l_row = acc_d[8] + __shfl_xor(acc_d[8], 32);
   const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
   const size_t obase = (((size_t)b * n + (row_ok ? row : 0)) * a.n_q_heads + head) * HD;
 #pragma unroll
