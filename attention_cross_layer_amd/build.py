@@ -48,6 +48,19 @@ def _run(cmd, verbose):
     return r
 
 
+# The plain streaming-read kernel bench.py sets the decode kernels against
+# (a measurement aid beside bench.py, not part of the library).
+READ_SRC = os.path.join(ROOT, "bench_read.hip")
+READ_LIB = os.path.join(ROOT, "bench_read.so")
+
+
+def build_read_probe(verbose: bool = False) -> str:
+    tmp = READ_LIB + ".tmp"
+    _run([HIPCC] + HIPFLAGS + ["-shared", READ_SRC, "-o", tmp], verbose)
+    os.replace(tmp, READ_LIB)
+    return READ_LIB
+
+
 def build(verbose: bool = False, jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cpp, hip = sources()
@@ -67,6 +80,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-fvisibility=hidden", "-o", tmp] + objs
          + ["-Wl,--no-undefined"], verbose)
     os.replace(tmp, LIB)
+    build_read_probe(verbose)
     return LIB
 
 

@@ -1051,6 +1051,16 @@ def decode_result(rig, args, cpu=True, step=True):
                                       "frac": b2 / (us2 * 1e-6) / 1e9 / HBM_PEAK_GBS,
                                       "bytes_per_launch": b2, "avg_launch_us": us2,
                                       "avg_call_us": call2}
+    ceil = read_ceiling(nbytes, rig.flush, rig.stream) if step else None
+    if ceil is not None:
+        res["roofline"]["read_ceiling"] = ceil
+        res["roofline"]["frac_of_read_ceiling"] = achieved / ceil["gbs"]
+    if step and "roofline_two_source" in res:
+        c2 = read_ceiling(res["roofline_two_source"]["bytes_per_launch"], rig.flush, rig.stream)
+        if c2 is not None:
+            res["roofline_two_source"]["read_ceiling_gbs"] = c2["gbs"]
+            res["roofline_two_source"]["frac_of_read_ceiling"] = (
+                res["roofline_two_source"]["achieved"] / c2["gbs"])
     if rig.fact and step:
         res["router"] = router_result(rig, pt, dom, args, us, call_us)
     traffic = recorded_traffic(wl.name)
@@ -1061,6 +1071,55 @@ def decode_result(rig, args, cpu=True, step=True):
         log(f"[bench] cpu baseline: {wl.name}")
         res["cpu_baseline"] = cpu_fact_decode(rig) if rig.fact else cpu_dense_decode(rig)
     return res
+
+
+READ_LAUNCH_SHAPES = [(blocks, u) for blocks in (256, 512, 1024, 2048, 4096) for u in (4, 8, 16)]
+
+
+def read_ceiling(nbytes, flush, stream, reps=5):
+    """What a plain read of the same bytes achieves on this GPU: the kernel of
+    bench_read.hip (block-contiguous 16-byte non-temporal loads, nothing
+    computed) over a buffer of ``nbytes``, cache flushed before each launch,
+    timed with events on the kernel itself, as the decode kernels are; the
+    median of ``reps`` launches for each of
+    READ_LAUNCH_SHAPES, the fastest shape reported.  None if the probe
+    library is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "bench_read.so")
+    if not os.path.exists(path):
+        log("[bench] bench_read.so not built: no read ceiling")
+        return None
+    lib = ctypes.CDLL(path)
+    lib.stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    n = (int(nbytes) + 15) // 16 * 16
+    buf = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(4096 * 256, dtype=torch.int32, device="cuda")
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    best = None
+    for blocks, u in READ_LAUNCH_SHAPES:
+        if lib.stream_read(buf.data_ptr(), n, sink.data_ptr(), blocks, u, sp, None, None) != 0:
+            raise RuntimeError("stream_read launch failed")
+        ev = []
+        for _ in range(reps):
+            flush.sum(dim=0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)      # creates the events; the launch records them again
+            e1.record(stream)
+            if lib.stream_read(buf.data_ptr(), n, sink.data_ptr(), blocks, u, sp,
+                               ctypes.c_void_p(e0.cuda_event), ctypes.c_void_p(e1.cuda_event)) != 0:
+                raise RuntimeError("stream_read launch failed")
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)[reps // 2]
+        if best is None or t < best[0]:
+            best = (t, blocks, u)
+    del buf, sink
+    t, blocks, u = best
+    return {"bytes": n, "us": t, "gbs": n / (t * 1e-6) / 1e9, "frac_of_peak": n / (t * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "launch": f"{blocks} workgroups x 256 threads, {u} loads in flight per thread",
+            "timing": "HIP events on the kernel's own start and end (median of %d launches, fastest of %d "
+                      "launch shapes), cache flushed" % (reps, len(READ_LAUNCH_SHAPES))}
 
 
 def router_result(rig, pt, dom, args, us, call_us):
@@ -1178,6 +1237,10 @@ def sweep_main(args):
                      "call_us": call_us, "bytes_per_call": nbytes}
                 for k in ("step_gbs", "step_gbs_cold", "kernel_gbs"):
                     p[k.replace("gbs", "frac")] = p[k] / HBM_PEAK_GBS
+                ceil = read_ceiling(nbytes, rig.flush, rig.stream, reps=3)
+                if ceil is not None:
+                    p["read_ceiling_gbs"] = ceil["gbs"]
+                    p["kernel_frac_of_read"] = p["kernel_gbs"] / ceil["gbs"]
                 points.append(p)
                 log(f"[sweep] {name} B={B} ctx={ctx}: {p['tokens_s']:.0f} tok/s, kernel "
                     f"{p['kernel_frac']:.1%} of HBM peak, cold step {p['step_frac_cold']:.1%}")
@@ -1186,14 +1249,17 @@ def sweep_main(args):
         del rig
     if args.sweep_out:
         lines = ["| workload | batch | ctx | splits | tok/s (warm) | step GB/s (% peak) | "
-                 "tok/s (cold) | cold step GB/s (% peak) | kernel us | kernel GB/s (% peak) |",
-                 "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+                 "tok/s (cold) | cold step GB/s (% peak) | kernel us | kernel GB/s (% peak) | "
+                 "plain read of the call's bytes, GB/s | kernel / plain read |",
+                 "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
         for p in points:
+            rd = (f"{p['read_ceiling_gbs']:,.0f} | {p['kernel_frac_of_read']:.1%}"
+                  if "read_ceiling_gbs" in p else "- | -")
             lines.append(f"| {p['workload']} | {p['batch']} | {p['ctx']} | {p['n_splits']} | "
                          f"{p['tokens_s']:,.0f} | {p['step_gbs']:,.0f} ({p['step_frac']:.1%}) | "
                          f"{p['tokens_s_cold']:,.0f} | {p['step_gbs_cold']:,.0f} "
                          f"({p['step_frac_cold']:.1%}) | {p['kernel_us']:.1f} | "
-                         f"{p['kernel_gbs']:,.0f} ({p['kernel_frac']:.1%}) |")
+                         f"{p['kernel_gbs']:,.0f} ({p['kernel_frac']:.1%}) | {rd} |")
         open(args.sweep_out, "w").write("\n".join(lines) + "\n")
     print(json.dumps({"metric": METRIC, "sweep": points}), flush=True)
 
