@@ -1208,6 +1208,19 @@ SWEEP = (("tinyllama_cla2", (1, 8, 16, 32, 64, 128), (512, 1024, 2048)),
          ("cla2_64k", (1, 2, 4, 8), (16384, 32768, 65536)))
 
 
+SWEEP_HEADER = """# Decode throughput per batch x context (one MI355X)
+
+Command (repository root):
+
+```
+python3 bench.py --sweep --steps 10 --warmup 3 --sweep-out profiles/decode_sweep_batch_ctx.md
+```
+
+Each row: one decode step over all layers (append + decode per layer), one token per sequence. *warm*: back-to-back steps. *cold*: the 256 MB Infinity Cache flushed before every layer's calls (flush outside the timed intervals). *kernel*: the single-source decode kernel alone, HIP events on its own start and end, cache flushed before each launch. Rates are algorithmic bytes (every source K/V tile read once) per second; % of the 8 TB/s HBM peak. *plain read*: `bench_read.hip` reading a buffer of the call's byte count once (block-contiguous 16-byte non-temporal loads, nothing computed), the same kernel events and cache flush, the fastest of 15 launch shapes (median of 3 launches each): what one launch that reads those bytes reaches on this GPU. `tinyllama_cla2`: 22 layers (11 owners), 32 q / 4 KV heads, hd 64. `cla2_64k`: 32 layers (16 owners), 32 q / 8 KV heads, hd 128, 1% of keys x4. Splits: the library's split-K partition count for the point.
+
+"""
+
+
 def sweep_main(args):
     if args.gpus != 1:
         print("bench.py runs on one GPU only", file=sys.stderr)
@@ -1260,7 +1273,7 @@ def sweep_main(args):
                          f"{p['tokens_s_cold']:,.0f} | {p['step_gbs_cold']:,.0f} "
                          f"({p['step_frac_cold']:.1%}) | {p['kernel_us']:.1f} | "
                          f"{p['kernel_gbs']:,.0f} ({p['kernel_frac']:.1%}) | {rd} |")
-        open(args.sweep_out, "w").write("\n".join(lines) + "\n")
+        open(args.sweep_out, "w").write(SWEEP_HEADER + "\n".join(lines) + "\n")
     print(json.dumps({"metric": METRIC, "sweep": points}), flush=True)
 
 
