@@ -175,11 +175,18 @@ extern "C" kvs_status kvs_cache_layout(const kvs_plan* plan, kvs_cache_sizes* ou
 // MI355X (cache flushed before each call):
 //  * the factorized kernel and the hd-64 bf16 MFMA kernel: one workgroup per
 //    CU (256); with S = 1 the merge launch disappears as well;
-//  * the VALU kernel (hd 128, fp32, two sources): one per CU when a call
-//    streams more than 384 MB, else four per CU (1024) with S <= 32: small
-//    calls are latency-bound and gain from more waves in flight (DepthGraft's
-//    8 x 8K batch: 70 -> 60 us per single-source layer), large ones lose.
+//  * the VALU kernel (hd 128, fp32, two sources): three workgroups per four
+//    CUs (192) when a call streams more than 384 MB, else four per CU (1024)
+//    with S <= 32: small calls are latency-bound and gain from more waves in
+//    flight (DepthGraft's 8 x 8K batch: 70 -> 60 us per single-source
+//    layer), large ones lose.  At 64K context fewer streams read HBM
+//    faster: 192 workgroups against 256, kernel alone, two alternations on
+//    one box: 154.1-155.8 vs 157.9-159.0 us at batch 4, 83.0-83.5 vs
+//    85.6-86.8 at batch 2, 302.8-303.3 vs 311.5-317.0 at batch 8 (224 and
+//    160 workgroups in between and below: 156.3-157.9, 173.0-174.0 at
+//    batch 4).
 static const int32_t kGroupsPerCu1 = 256;
+static const int32_t kGroupsLarge = 192;
 static const int32_t kGroupsPerCu4 = 1024;
 static const double kSmallCallBytes = 384.0 * (1 << 20);
 
@@ -199,6 +206,8 @@ extern "C" kvs_status kvs_decode_splits(const kvs_plan* plan, int32_t batch, int
     if (call_bytes <= kSmallCallBytes) {
       target = kGroupsPerCu4;
       s_max = 32;
+    } else {
+      target = kGroupsLarge;
     }
   }
   int32_t s = (target + groups - 1) / groups;

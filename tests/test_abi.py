@@ -140,8 +140,8 @@ def test_decode_split_choice_and_workspace():
     src, w = datagen.share_map(wl)
     plan = K.kvs_share_plan(_cfg(32, 32, 8, 128, "bf16", 4, 65536), src, w)
     s = K.kvs_decode_splits(plan, 4, 65536)
-    # one 4-wave workgroup per (partition, KV head, sequence): about 256 of them
-    assert 1 <= s <= 64 and 4 * 8 * s >= 256
+    # one 4-wave workgroup per (partition, KV head, sequence): about 192 of them
+    assert 1 <= s <= 64 and 4 * 8 * s >= 192
     assert K.kvs_decode_splits(plan, 4, 64) == 1
     # partials [B][Hq][S][hd], maxima and sums [B][Hq][S]
     assert K.kvs_decode_workspace_size(plan, 4, s) == 4 * 32 * s * (128 + 2) * 4
@@ -152,11 +152,13 @@ def test_decode_split_choice_and_workspace():
 
 
 def test_decode_split_rule_by_kernel_and_call_size():
-    # VALU kernel (hd 128): a call streaming 1 GiB keeps one workgroup per CU
-    # (4 x 8 x 8 = 256), one of 256 MiB takes four per CU (8 x 8 x 16 = 1024)
+    # VALU kernel (hd 128): a call streaming 1 GiB takes three workgroups per
+    # four CUs (4 x 8 x 6 = 192), one of 256 MiB four per CU (8 x 8 x 16 = 1024)
     src, w = datagen.share_map(datagen.WORKLOADS["cla2_64k"])
     plan = K.kvs_share_plan(_cfg(32, 32, 8, 128, "bf16", 8, 65536), src, w)
-    assert K.kvs_decode_splits(plan, 4, 65536) == 8
+    assert K.kvs_decode_splits(plan, 4, 65536) == 6
+    assert K.kvs_decode_splits(plan, 2, 65536) == 12
+    assert K.kvs_decode_splits(plan, 8, 65536) == 3
     assert K.kvs_decode_splits(plan, 8, 8192) == 16
     # at most 32 partitions on the small-call path, at least 4 pages each
     assert K.kvs_decode_splits(plan, 1, 65536) == 32
