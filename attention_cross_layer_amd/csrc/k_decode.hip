@@ -504,16 +504,22 @@ struct MfmaPage {
 };
 
 // Waves per workgroup (one workgroup per (partition, KV head, sequence)).
-// Each wave loads one page and computes it before loading the next: with
+// Each wave loads one page and computes it before loading the next.  With
 // 256 workgroups of 4 waves that keeps 16 MB in flight, and the streaming
 // rate is higher than with a second page in flight per wave (26.7 vs
 // 28.4 us per tinyllama_cla2 layer) or with 8 or 2 waves (27.4, 30.4 us):
 // more requests in flight lower the HBM efficiency, fewer leave it idle.
-constexpr int kMfmaWaves = 4;
+// From one workgroup per CU up, three waves stream faster still (batch 64 x
+// 2K: 26.0-26.5 vs 26.6-26.9 us; 128 x 2K: 49.5 vs 51.1-51.4; 128 x 512:
+// 16.2-16.4 vs 17.4-17.5), while smaller grids lose with three (8 x 512:
+// 7.6-7.7 vs 6.5-6.7), so the launcher takes NW = 3 for grids of at least
+// 256 workgroups and 4 below.
+constexpr int kMfmaWavesSmall = 4;
+constexpr int kMfmaWavesLarge = 3;
+constexpr int kMfmaLargeGrid = 256;
 
-template <int G>
-__global__ __launch_bounds__(64 * kMfmaWaves) void decode_mfma_kernel(DecodeParams a) {
-  constexpr int NW = kMfmaWaves;
+template <int G, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams a) {
   constexpr int HD = 64;
   static_assert(G <= 16, "one 16-column block of heads");
   __shared__ float mrg_o[NW][G][HD];
@@ -707,7 +713,10 @@ __global__ __launch_bounds__(64 * kMfmaWaves) void decode_mfma_kernel(DecodePara
 template <int G>
 int run_decode_mfma(const DecodeParams& p, int B, hipStream_t st, const KernelEvents& ev) {
   dim3 grid(p.n_splits, p.n_kv_heads, B);
-  launch_main(ev, decode_mfma_kernel<G>, grid, dim3(64 * kMfmaWaves), st, p);
+  if ((long long)p.n_splits * p.n_kv_heads * B >= kMfmaLargeGrid)
+    launch_main(ev, decode_mfma_kernel<G, kMfmaWavesLarge>, grid, dim3(64 * kMfmaWavesLarge), st, p);
+  else
+    launch_main(ev, decode_mfma_kernel<G, kMfmaWavesSmall>, grid, dim3(64 * kMfmaWavesSmall), st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return (int)e;
   hipLaunchKernelGGL((decode_merge_kernel<G, 64>), dim3(p.n_kv_heads, B), dim3(256), 0, st, p);
