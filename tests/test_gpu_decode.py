@@ -27,6 +27,11 @@ CASES = {
     "g2_hd128_f32": (W["tiny_cla2"].with_(n_q_heads=4, head_dim=128), 2, 190, [190, 3]),
     "g8_hd128_mixed": (W["depthgraft"].with_(n_layers=6, dg_stride=2, n_q_heads=64), 1, 250, [250]),
     "g4_hd64_f32_mixed": (W["depthgraft"].with_(n_layers=6, dg_stride=2, head_dim=64, dtype="f32"), 2, 99, [99, 64]),
+    # 64 sequences x 4 KV heads: a grid of 256 workgroups, where the hd-64 MFMA
+    # decode runs three waves per workgroup (pages w, w+3, ...); ragged and
+    # empty sequences
+    "mfma_three_wave_grid": (W["tinyllama_cla2"].with_(n_layers=2), 64, 300,
+                             [0, 1, 2, 63, 64, 65] + [(37 * i) % 300 + 1 for i in range(6, 63)] + [300]),
 }
 
 
@@ -56,6 +61,18 @@ def test_split_count_sweep_agrees():
         outs.append(got.double().cpu())
     for o in outs[1:]:
         assert float((o - outs[0]).abs().max()) < 2e-3
+
+
+def test_three_wave_mfma_decode_across_split_counts():
+    # grids of 256, 512 and 768 workgroups (S = 1, 2, 3): three waves each
+    wl, B, ctx, lens = CASES["mfma_three_wave_grid"]
+    d = Dense(wl, B, ctx, lens)
+    ref = d.oracle_decode(1)
+    for s in (1, 2, 3):
+        note(f"[three-wave grid] n_splits={s}")
+        got = d.decode(1, n_splits=s)
+        torch.cuda.synchronize()
+        assert_close(got, ref, wl.dtype, f"three-wave grid, n_splits={s}")
 
 
 def test_deterministic_and_page_permutation_invariant():
