@@ -459,20 +459,23 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams a) {
 }
 
 // ---------------------------------------------------------------- MFMA path
-// bf16, hd 64, one source, G <= 16: both products of a page on
-// v_mfma_f32_16x16x32_bf16 (A: lane l holds row l%16, k = 8(l/16)..+7;
-// B: column l%16, same k; result register r of lane l is row 4(l/16)+r,
-// column l%16), reading the cache in its stored layouts:
-//   scores  S[keys][heads] = K q^T: A = 16 keys x 32 dims, one 16-byte load of
-//           a K row per lane; B = the G queries (columns >= G zero), in
-//           registers for the whole launch.  Lane (g = l/16, h = l%16) ends
-//           with keys 16kb + 4g + r (kb = 0..3, r = 0..3) of head h.
+// bf16, one source, hd 64 with G <= 32 or hd 128 with G = 16: both products
+// of a page on v_mfma_f32_16x16x32_bf16 (A: lane l holds row l%16,
+// k = 8(l/16)..+7; B: column l%16, same k; result register r of lane l is
+// row 4(l/16)+r, column l%16), reading the cache in its stored layouts:
+//   scores  S[keys][heads] = K q^T per block of 16 heads: A = 16 keys x 32
+//           dims, one 16-byte load of a K row chunk per lane; B = 16 queries of the
+//           group (columns past G zero), in registers for the whole launch.
+//           Lane (g = l/16, h = l%16) ends with keys 16kb + 4g + r (kb =
+//           0..3, r = 0..3) of head h of each block.
 //   values  O[heads][dims] = P^T V over 32 keys per step, the keys of step ps
 //           taken in the order those registers hold them:
 //           k = 8g + e  ->  key 32ps + 16(e/4) + 4g + e%4,
 //           so P^T is the lane's own (bf16) probabilities and the matching V
 //           operand is 4 dwords of the pair-interleaved V page (each dword =
 //           one dim of two consecutive keys).
+// Every K and V tile is loaded once for all G heads: a group of 32 (hd 64)
+// runs two 16-head blocks over the same page registers.
 // The online softmax keeps one running maximum per head (raw scores; the
 // positive scale is applied inside the exponent), so only heads whose
 // maximum moved rescale their accumulators.
@@ -498,9 +501,10 @@ __device__ __forceinline__ float row_max4(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+template <int HD>
 struct MfmaPage {
-  uint4 k[4][2];      // [kb][ks]: key 16kb + l%16, dims 8(l/16) + 32ks .. +7
-  uint4 v[2][4];      // [ps][db]: 4 dwords (pairs) of dim 16db + l%16
+  uint4 k[4][HD / 32];   // [kb][ks]: key 16kb + l%16, dims 8(l/16) + 32ks .. +7
+  uint4 v[2][HD / 16];   // [ps][db]: 4 dwords (pairs) of dim 16db + l%16
 };
 
 // Waves per workgroup (one workgroup per (partition, KV head, sequence)).
@@ -518,10 +522,12 @@ constexpr int kMfmaWavesSmall = 4;
 constexpr int kMfmaWavesLarge = 3;
 constexpr int kMfmaLargeGrid = 256;
 
-template <int G, int NW>
+template <int G, int HD, int NW>
 __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams a) {
-  constexpr int HD = 64;
-  static_assert(G <= 16, "one 16-column block of heads");
+  constexpr int GB = (G + 15) / 16;          // 16-head blocks
+  constexpr int KS = HD / 32;                // 32-dim steps of the scores
+  constexpr int DB = HD / 16;                // 16-dim blocks of the values
+  static_assert(G <= 32 && (HD == 64 || HD == 128), "shapes of the MFMA decode");
   __shared__ float mrg_o[NW][G][HD];
   __shared__ float mrg_m[NW][G];
   __shared__ float mrg_l[NW][G];
@@ -533,15 +539,17 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams a) {
   const int S = a.n_splits;
   const int col = lane & 15, g = lane >> 4;
 
-  // B operand of the scores: head `col`, dims 8g + 32ks .. +7
-  uint4 qf[2];
-  {
-    const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) +
-                         ((size_t)b * a.n_q_heads + (size_t)kvh * G + (col < G ? col : 0)) * HD;
+  // B operands of the scores: head 16gb + col, dims 8g + 32ks .. +7
+  uint4 qf[GB][KS];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+  for (int gb = 0; gb < GB; ++gb) {
+    const int h = 16 * gb + col;
+    const uint16_t* qh = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((size_t)b * a.n_q_heads + (size_t)kvh * G + (h < G ? h : 0)) * HD;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
       const uint4 x = *reinterpret_cast<const uint4*>(qh + 8 * g + 32 * ks);
-      qf[ks] = col < G ? x : make_uint4(0, 0, 0, 0);
+      qf[gb][ks] = h < G ? x : make_uint4(0, 0, 0, 0);
     }
   }
 
@@ -558,19 +566,21 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams a) {
     while (p < pe && (unsigned)pt[p] >= (unsigned)a.n_phys_pages) p += NW;
     return p;
   };
-  auto load = [&](int pg, MfmaPage& r) {
+  auto load = [&](int pg, MfmaPage<HD>& r) {
     const int64_t tile = ((int64_t)pt[pg] * a.n_kv_heads + kvh) * (kPage * HD);
     const uint16_t* kt = kbase + tile;
-    const uint32_t* vt = reinterpret_cast<const uint32_t*>(vbase + tile);   // [32 pairs][64 dims]
+    const uint32_t* vt = reinterpret_cast<const uint32_t*>(vbase + tile);   // [32 pairs][HD dims]
+    // 16-byte chunk g + 4ks of key 16kb + col, at its place in the K page
+    // layout (row-major at hd 64)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        r.k[kb][ks] = *reinterpret_cast<const uint4*>(kt + (16 * kb + col) * HD + 8 * g + 32 * ks);
+      for (int ks = 0; ks < KS; ++ks)
+        r.k[kb][ks] = *reinterpret_cast<const uint4*>(kt + k_chunk_offset(16 * kb + col, g + 4 * ks, HD / 8, 8));
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < DB; ++db) {
         const int d = 16 * db + col;
         const int p0 = 16 * ps + 2 * g, p1 = p0 + 8;           // pairs of keys 32ps+4g.., 32ps+16+4g..
         r.v[ps][db] = make_uint4(vt[p0 * HD + d], vt[(p0 + 1) * HD + d], vt[p1 * HD + d],
@@ -578,60 +588,19 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams a) {
       }
   };
 
-  float m_run = -INFINITY, l_run = 0.f;   // for head `col`, over this lane's keys
-  f32x4_t o[4];
+  float m_run[GB], l_run[GB];   // for head 16gb + col, over this lane's keys
+  f32x4_t o[GB][DB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int gb = 0; gb < GB; ++gb) {
+    m_run[gb] = -INFINITY;
+    l_run[gb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[gb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   const uint32_t ones = 0x3F803F80u;       // (1.0, 1.0) in bf16
 
-  auto compute = [&](int pg, MfmaPage& r) {
+  auto compute = [&](int pg, MfmaPage<HD>& r) {
     const int nvalid = n_keys - pg * kPage;
-    f32x4_t s[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = mfma16(r.k[kb][0], qf[0], f32x4_t{0.f, 0.f, 0.f, 0.f});
-      s[kb] = mfma16(r.k[kb][1], qf[1], s[kb]);
-    }
-    if (nvalid < kPage || G < 16) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          s[kb][e] = (col < G && 16 * kb + 4 * g + e < nvalid) ? s[kb][e] : -INFINITY;
-    }
-    float mt = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
-#pragma unroll
-    for (int kb = 1; kb < 4; ++kb) mt = fmaxf(mt, fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3])));
-    mt = row_max4(mt);
-    const float mn = fmaxf(m_run, mt);
-    const float neg = mn == -INFINITY ? 0.f : -mn * a.scale_log2;
-    const float alpha = m_run == mn ? 1.f : dev::fast_exp2(fmaf(m_run, a.scale_log2, neg));
-    m_run = mn;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-      // accumulator entry rr of lane l belongs to head 4(l/16) + rr
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const float f = __shfl(alpha, 4 * g + rr);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) o[db][rr] *= f;
-      }
-      l_run *= alpha;
-    }
-    uint4 pf[2];
-#pragma unroll
-    for (int ps = 0; ps < 2; ++ps) {
-      const f32x4_t& s0 = s[2 * ps];
-      const f32x4_t& s1 = s[2 * ps + 1];
-      pf[ps].x = pack_bf16_rne(dev::fast_exp2(fmaf(s0[0], a.scale_log2, neg)), dev::fast_exp2(fmaf(s0[1], a.scale_log2, neg)));
-      pf[ps].y = pack_bf16_rne(dev::fast_exp2(fmaf(s0[2], a.scale_log2, neg)), dev::fast_exp2(fmaf(s0[3], a.scale_log2, neg)));
-      pf[ps].z = pack_bf16_rne(dev::fast_exp2(fmaf(s1[0], a.scale_log2, neg)), dev::fast_exp2(fmaf(s1[1], a.scale_log2, neg)));
-      pf[ps].w = pack_bf16_rne(dev::fast_exp2(fmaf(s1[2], a.scale_log2, neg)), dev::fast_exp2(fmaf(s1[3], a.scale_log2, neg)));
-      // the running sum adds the same bf16-rounded probabilities
-      l_run = dot2_bf16(pf[ps].x, ones, l_run);
-      l_run = dot2_bf16(pf[ps].y, ones, l_run);
-      l_run = dot2_bf16(pf[ps].z, ones, l_run);
-      l_run = dot2_bf16(pf[ps].w, ones, l_run);
-    }
     if (nvalid < kPage) {
       // keys past the sequence end: p = 0, but unwritten V memory may hold NaN
       // patterns and 0 * NaN is NaN
@@ -643,7 +612,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams a) {
         const uint32_t m2 = (k1 < nvalid ? 0x0000ffffu : 0u) | (k1 + 1 < nvalid ? 0xffff0000u : 0u);
         const uint32_t m3 = (k1 + 2 < nvalid ? 0x0000ffffu : 0u) | (k1 + 3 < nvalid ? 0xffff0000u : 0u);
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
+        for (int db = 0; db < DB; ++db) {
           r.v[ps][db].x &= m0;
           r.v[ps][db].y &= m1;
           r.v[ps][db].z &= m2;
@@ -652,32 +621,84 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams a) {
       }
     }
 #pragma unroll
-    for (int ps = 0; ps < 2; ++ps)
+    for (int gb = 0; gb < GB; ++gb) {
+      f32x4_t s[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) o[db] = mfma16(pf[ps], r.v[ps][db], o[db]);
+      for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = mfma16(r.k[kb][0], qf[gb][0], f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int ks = 1; ks < KS; ++ks) s[kb] = mfma16(r.k[kb][ks], qf[gb][ks], s[kb]);
+      }
+      if (nvalid < kPage || 16 * gb + 16 > G) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            s[kb][e] = (16 * gb + col < G && 16 * kb + 4 * g + e < nvalid) ? s[kb][e] : -INFINITY;
+      }
+      float mt = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+      for (int kb = 1; kb < 4; ++kb) mt = fmaxf(mt, fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3])));
+      mt = row_max4(mt);
+      const float mn = fmaxf(m_run[gb], mt);
+      const float neg = mn == -INFINITY ? 0.f : -mn * a.scale_log2;
+      const float alpha = m_run[gb] == mn ? 1.f : dev::fast_exp2(fmaf(m_run[gb], a.scale_log2, neg));
+      m_run[gb] = mn;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+        // accumulator entry rr of lane l belongs to head 16gb + 4(l/16) + rr
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float f = __shfl(alpha, 4 * g + rr);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) o[gb][db][rr] *= f;
+        }
+        l_run[gb] *= alpha;
+      }
+      uint4 pf[2];
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps) {
+        const f32x4_t& s0 = s[2 * ps];
+        const f32x4_t& s1 = s[2 * ps + 1];
+        pf[ps].x = pack_bf16_rne(dev::fast_exp2(fmaf(s0[0], a.scale_log2, neg)), dev::fast_exp2(fmaf(s0[1], a.scale_log2, neg)));
+        pf[ps].y = pack_bf16_rne(dev::fast_exp2(fmaf(s0[2], a.scale_log2, neg)), dev::fast_exp2(fmaf(s0[3], a.scale_log2, neg)));
+        pf[ps].z = pack_bf16_rne(dev::fast_exp2(fmaf(s1[0], a.scale_log2, neg)), dev::fast_exp2(fmaf(s1[1], a.scale_log2, neg)));
+        pf[ps].w = pack_bf16_rne(dev::fast_exp2(fmaf(s1[2], a.scale_log2, neg)), dev::fast_exp2(fmaf(s1[3], a.scale_log2, neg)));
+        // the running sum adds the same bf16-rounded probabilities
+        l_run[gb] = dot2_bf16(pf[ps].x, ones, l_run[gb]);
+        l_run[gb] = dot2_bf16(pf[ps].y, ones, l_run[gb]);
+        l_run[gb] = dot2_bf16(pf[ps].z, ones, l_run[gb]);
+        l_run[gb] = dot2_bf16(pf[ps].w, ones, l_run[gb]);
+      }
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[gb][db] = mfma16(pf[ps], r.v[ps][db], o[gb][db]);
+    }
   };
 
-  MfmaPage bufA;
+  MfmaPage<HD> bufA;
   for (int pg = next_page(pb + wave); pg < pe; pg = next_page(pg + NW)) {
     load(pg, bufA);
     compute(pg, bufA);
   }
 
   // ---- this wave's (O, m, l) to LDS; m in log2 units as the merge expects
-  {
-    float l = l_run;
+#pragma unroll
+  for (int gb = 0; gb < GB; ++gb) {
+    float l = l_run[gb];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    if (g == 0 && col < G) {
-      mrg_m[wave][col] = m_run == -INFINITY ? -INFINITY : m_run * a.scale_log2;
-      mrg_l[wave][col] = l;
+    const int hc = 16 * gb + col;
+    if (g == 0 && hc < G) {
+      mrg_m[wave][hc] = m_run[gb] == -INFINITY ? -INFINITY : m_run[gb] * a.scale_log2;
+      mrg_l[wave][hc] = l;
     }
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int h = 4 * g + rr;
-        if (h < G) mrg_o[wave][h][16 * db + col] = o[db][rr];
+        const int h = 16 * gb + 4 * g + rr;
+        if (h < G) mrg_o[wave][h][16 * db + col] = o[gb][db][rr];
       }
   }
   __syncthreads();
@@ -710,28 +731,40 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams a) {
   }
 }
 
-template <int G>
+template <int G, int HD>
 int run_decode_mfma(const DecodeParams& p, int B, hipStream_t st, const KernelEvents& ev) {
   dim3 grid(p.n_splits, p.n_kv_heads, B);
   if ((long long)p.n_splits * p.n_kv_heads * B >= kMfmaLargeGrid)
-    launch_main(ev, decode_mfma_kernel<G, kMfmaWavesLarge>, grid, dim3(64 * kMfmaWavesLarge), st, p);
+    launch_main(ev, decode_mfma_kernel<G, HD, kMfmaWavesLarge>, grid, dim3(64 * kMfmaWavesLarge), st, p);
   else
-    launch_main(ev, decode_mfma_kernel<G, kMfmaWavesSmall>, grid, dim3(64 * kMfmaWavesSmall), st, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.n_splits == 1) return (int)e;
-  hipLaunchKernelGGL((decode_merge_kernel<G, 64>), dim3(p.n_kv_heads, B), dim3(256), 0, st, p);
-  return (int)hipGetLastError();
-}
-
-template <typename T, int HD, int G, int NSRC>
-int run_decode(const DecodeParams& p, int B, hipStream_t st, const KernelEvents& ev) {
-  if constexpr (sizeof(T) == 2 && HD == 64 && NSRC == 1 && G <= 16) return run_decode_mfma<G>(p, B, st, ev);
-  dim3 grid(p.n_splits, p.n_kv_heads, B);
-  launch_main(ev, decode_kernel<T, HD, G, NSRC>, grid, dim3(256), st, p);
+    launch_main(ev, decode_mfma_kernel<G, HD, kMfmaWavesSmall>, grid, dim3(64 * kMfmaWavesSmall), st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_splits == 1) return (int)e;
   hipLaunchKernelGGL((decode_merge_kernel<G, HD>), dim3(p.n_kv_heads, B), dim3(256), 0, st, p);
   return (int)hipGetLastError();
+}
+
+// Which single-source bf16 calls take the MFMA decode: hd 64 up to G = 32,
+// hd 128 at G = 16 (the dot-product kernel would hold 16 heads' queries
+// beside a page: 512 registers and spills).  Smaller hd-128 groups stream
+// faster through the dot-product kernel.
+template <typename T, int HD, int G, int NSRC>
+constexpr bool use_mfma_decode() {
+  return sizeof(T) == 2 && NSRC == 1 && ((HD == 64 && G <= 32) || (HD == 128 && G == 16));
+}
+
+template <typename T, int HD, int G, int NSRC>
+int run_decode(const DecodeParams& p, int B, hipStream_t st, const KernelEvents& ev) {
+  if constexpr (use_mfma_decode<T, HD, G, NSRC>()) {
+    return run_decode_mfma<G, HD>(p, B, st, ev);
+  } else {
+    dim3 grid(p.n_splits, p.n_kv_heads, B);
+    launch_main(ev, decode_kernel<T, HD, G, NSRC>, grid, dim3(256), st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.n_splits == 1) return (int)e;
+    hipLaunchKernelGGL((decode_merge_kernel<G, HD>), dim3(p.n_kv_heads, B), dim3(256), 0, st, p);
+    return (int)hipGetLastError();
+  }
 }
 
 typedef int (*DecodeFn)(const DecodeParams&, int, hipStream_t, const KernelEvents&);

@@ -173,8 +173,9 @@ extern "C" kvs_status kvs_cache_layout(const kvs_plan* plan, kvs_cache_sizes* ou
 // KV head, sequence), and at least 4 pages (one per wave) per partition, at
 // most max_decode_splits() partitions.  Targets, from split sweeps on one
 // MI355X (cache flushed before each call):
-//  * the factorized kernel and the hd-64 bf16 MFMA kernel: one workgroup per
-//    CU (256); with S = 1 the merge launch disappears as well;
+//  * the factorized kernel and the bf16 MFMA kernel (hd 64, and hd 128 at
+//    G = 16): one workgroup per CU (256); with S = 1 the merge launch
+//    disappears as well;
 //  * the VALU kernel (hd 128, fp32, two sources): three workgroups per four
 //    CUs (192) when a call streams more than 384 MB, else four per CU (1024)
 //    with S <= 32: small calls are latency-bound and gain from more waves in
@@ -199,7 +200,8 @@ extern "C" kvs_status kvs_decode_splits(const kvs_plan* plan, int32_t batch, int
   int32_t seq = max_seq_len < 1 ? 1 : (max_seq_len > c.max_ctx ? c.max_ctx : max_seq_len);
   const int32_t pages = (seq + kPage - 1) / kPage;
   const int32_t groups = batch * c.n_kv_heads;
-  const bool mfma_kernel = c.dtype == KVS_BF16 && c.head_dim == 64 && c.n_q_heads / c.n_kv_heads <= 16;
+  const int32_t G = c.n_q_heads / c.n_kv_heads;
+  const bool mfma_kernel = c.dtype == KVS_BF16 && ((c.head_dim == 64 && G <= 32) || (c.head_dim == 128 && G == 16));
   int32_t target = kGroupsPerCu1, s_max = max_decode_splits();
   if (c.kind == KVS_DENSE && !mfma_kernel) {
     const double call_bytes = double(groups) * pages * kPage * c.head_dim * 2 * elem_bytes(c.dtype);

@@ -75,6 +75,26 @@ def test_three_wave_mfma_decode_across_split_counts():
         assert_close(got, ref, wl.dtype, f"three-wave grid, n_splits={s}")
 
 
+@pytest.mark.parametrize("name,wl,B,ctx", [
+    # 32 query heads on one KV head (hd 64) and 16 on one (hd 128): the MFMA
+    # decode with two 16-head blocks over one page load, and at hd 128
+    ("g32_hd64", W["tinyllama_cla2"].with_(n_layers=2, n_kv_heads=1), 64, 200),
+    ("g16_hd128", W["cla2_64k"].with_(n_layers=2, n_q_heads=16, n_kv_heads=1), 64, 200),
+])
+def test_large_group_mfma_decode(name, wl, B, ctx):
+    lens = [ctx if i % 7 == 0 else (29 * i) % ctx + 1 for i in range(B)]
+    lens[3] = 0
+    d = Dense(wl, B, ctx, lens)
+    ref = d.oracle_decode(1)
+    # 1 and 3 partitions: grids of 64 (four waves) and 192 workgroups; 4 and
+    # 5: 256 and 320 (three waves)
+    for s in (1, 3, 4, 5):
+        note(f"[large group] {name} n_splits={s}")
+        got = d.decode(1, n_splits=s)
+        torch.cuda.synchronize()
+        assert_close(got, ref, wl.dtype, f"{name}, n_splits={s}")
+
+
 def test_deterministic_and_page_permutation_invariant():
     wl, B, ctx, lens = CASES["tinyllama_shape_ragged"]
     d = Dense(wl, B, ctx, lens)
