@@ -205,9 +205,14 @@ extern "C" kvs_status kvs_decode_splits(const kvs_plan* plan, int32_t batch, int
   int32_t target = kGroupsPerCu1, s_max = max_decode_splits();
   if (c.kind == KVS_DENSE && !mfma_kernel) {
     const double call_bytes = double(groups) * pages * kPage * c.head_dim * 2 * elem_bytes(c.dtype);
-    if (call_bytes <= kSmallCallBytes) {
+    if (call_bytes <= kSmallCallBytes && G < 8) {
       target = kGroupsPerCu4;
       s_max = 32;
+    } else if (call_bytes <= kSmallCallBytes) {
+      // groups of 8 hold one wave per SIMD: more workgroups than CUs only
+      // queue (8 heads at hd 128, batch 4 x 16K: 52.0, 55.9, 65.1 us at
+      // 256, 512, 1024 workgroups)
+      target = kGroupsPerCu1;
     } else {
       target = kGroupsLarge;
     }

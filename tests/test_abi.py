@@ -163,6 +163,10 @@ def test_decode_split_rule_by_kernel_and_call_size():
     # at most 32 partitions on the small-call path, at least 4 pages each
     assert K.kvs_decode_splits(plan, 1, 65536) == 32
     assert K.kvs_decode_splits(plan, 8, 512) == 2
+    # a group of 8 at hd 128 runs one wave per SIMD: one workgroup per CU
+    # for a small call too (4 x 8 x 8 = 256)
+    plan8 = K.kvs_share_plan(_cfg(32, 64, 8, 128, "bf16", 8, 65536), src, w)
+    assert K.kvs_decode_splits(plan8, 4, 16384) == 8
     # hd-64 bf16 MFMA kernel: one workgroup per CU
     src, w = datagen.share_map(datagen.WORKLOADS["tinyllama_cla2"])
     plan = K.kvs_share_plan(_cfg(22, 32, 4, 64, "bf16", 64, 2048), src, w)
