@@ -566,17 +566,20 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams a) {
     while (p < pe && (unsigned)pt[p] >= (unsigned)a.n_phys_pages) p += NW;
     return p;
   };
+  const int k_lane = ((col / 8) * (HD / 64) * kPage + (col % 8) * 8 + g) * 8;
   auto load = [&](int pg, MfmaPage<HD>& r) {
     const int64_t tile = ((int64_t)pt[pg] * a.n_kv_heads + kvh) * (kPage * HD);
     const uint16_t* kt = kbase + tile;
     const uint32_t* vt = reinterpret_cast<const uint32_t*>(vbase + tile);   // [32 pairs][HD dims]
-    // 16-byte chunk g + 4ks of key 16kb + col, at its place in the K page
-    // layout (row-major at hd 64)
+    // 16-byte chunk c = g + 4ks of key t = 16kb + col at its place in the K
+    // page layout, k_chunk_offset(t, c, HD/8, 8) split into this lane's part
+    // and a constant per (kb, ks) (row-major at hd 64)
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        r.k[kb][ks] = *reinterpret_cast<const uint4*>(kt + k_chunk_offset(16 * kb + col, g + 4 * ks, HD / 8, 8));
+        r.k[kb][ks] = *reinterpret_cast<const uint4*>(
+            kt + k_lane + ((2 * kb * (HD / 64) + ks / 2) * kPage + 4 * (ks % 2)) * 8);
 #pragma unroll
     for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
@@ -601,25 +604,6 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams a) {
 
   auto compute = [&](int pg, MfmaPage<HD>& r) {
     const int nvalid = n_keys - pg * kPage;
-    if (nvalid < kPage) {
-      // keys past the sequence end: p = 0, but unwritten V memory may hold NaN
-      // patterns and 0 * NaN is NaN
-#pragma unroll
-      for (int ps = 0; ps < 2; ++ps) {
-        const int k0 = 32 * ps + 4 * g, k1 = k0 + 16;
-        const uint32_t m0 = (k0 < nvalid ? 0x0000ffffu : 0u) | (k0 + 1 < nvalid ? 0xffff0000u : 0u);
-        const uint32_t m1 = (k0 + 2 < nvalid ? 0x0000ffffu : 0u) | (k0 + 3 < nvalid ? 0xffff0000u : 0u);
-        const uint32_t m2 = (k1 < nvalid ? 0x0000ffffu : 0u) | (k1 + 1 < nvalid ? 0xffff0000u : 0u);
-        const uint32_t m3 = (k1 + 2 < nvalid ? 0x0000ffffu : 0u) | (k1 + 3 < nvalid ? 0xffff0000u : 0u);
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          r.v[ps][db].x &= m0;
-          r.v[ps][db].y &= m1;
-          r.v[ps][db].z &= m2;
-          r.v[ps][db].w &= m3;
-        }
-      }
-    }
 #pragma unroll
     for (int gb = 0; gb < GB; ++gb) {
       f32x4_t s[4];
@@ -668,6 +652,26 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams a) {
         l_run[gb] = dot2_bf16(pf[ps].y, ones, l_run[gb]);
         l_run[gb] = dot2_bf16(pf[ps].z, ones, l_run[gb]);
         l_run[gb] = dot2_bf16(pf[ps].w, ones, l_run[gb]);
+      }
+      if (gb == 0 && nvalid < kPage) {
+        // keys past the sequence end: p = 0, but unwritten V memory may hold
+        // NaN patterns and 0 * NaN is NaN.  Masked here, after the scores,
+        // so that the scores wait only for K while V is still in flight.
+#pragma unroll
+        for (int ps = 0; ps < 2; ++ps) {
+          const int k0 = 32 * ps + 4 * g, k1 = k0 + 16;
+          const uint32_t m0 = (k0 < nvalid ? 0x0000ffffu : 0u) | (k0 + 1 < nvalid ? 0xffff0000u : 0u);
+          const uint32_t m1 = (k0 + 2 < nvalid ? 0x0000ffffu : 0u) | (k0 + 3 < nvalid ? 0xffff0000u : 0u);
+          const uint32_t m2 = (k1 < nvalid ? 0x0000ffffu : 0u) | (k1 + 1 < nvalid ? 0xffff0000u : 0u);
+          const uint32_t m3 = (k1 + 2 < nvalid ? 0x0000ffffu : 0u) | (k1 + 3 < nvalid ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            r.v[ps][db].x &= m0;
+            r.v[ps][db].y &= m1;
+            r.v[ps][db].z &= m2;
+            r.v[ps][db].w &= m3;
+          }
+        }
       }
 #pragma unroll
       for (int ps = 0; ps < 2; ++ps)
