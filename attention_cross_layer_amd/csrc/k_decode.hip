@@ -513,11 +513,13 @@ struct MfmaPage {
 // rate is higher than with a second page in flight per wave (26.7 vs
 // 28.4 us per tinyllama_cla2 layer) or with 8 or 2 waves (27.4, 30.4 us):
 // more requests in flight lower the HBM efficiency, fewer leave it idle.
-// From one workgroup per CU up, three waves stream faster still (batch 64 x
-// 2K: 26.0-26.5 vs 26.6-26.9 us; 128 x 2K: 49.5 vs 51.1-51.4; 128 x 512:
-// 16.2-16.4 vs 17.4-17.5), while smaller grids lose with three (8 x 512:
-// 7.6-7.7 vs 6.5-6.7), so the launcher takes NW = 3 for grids of at least
-// 256 workgroups and 4 below.
+// Unsplit launches of at least one workgroup per CU stream faster still
+// with three waves (batch 64 x 2K: 26.0-26.5 vs 26.6-26.9 us; 128 x 2K:
+// 49.5 vs 51.1-51.4; 128 x 512: 16.2-16.4 vs 17.4-17.5), while smaller
+// grids (8 x 512: 7.6-7.7 vs 6.5-6.7) and split ones (32 x 2K at S = 2:
+// 18.2 vs 17.5; 16 x 1K at S = 4: 8.4-8.5 vs 7.5-7.7) lose with three, so
+// the launcher takes NW = 3 for unsplit grids of at least 256 workgroups
+// and 4 otherwise.
 constexpr int kMfmaWavesSmall = 4;
 constexpr int kMfmaWavesLarge = 3;
 constexpr int kMfmaLargeGrid = 256;
@@ -738,7 +740,7 @@ __global__ __launch_bounds__(64 * NW) void decode_mfma_kernel(DecodeParams a) {
 template <int G, int HD>
 int run_decode_mfma(const DecodeParams& p, int B, hipStream_t st, const KernelEvents& ev) {
   dim3 grid(p.n_splits, p.n_kv_heads, B);
-  if ((long long)p.n_splits * p.n_kv_heads * B >= kMfmaLargeGrid)
+  if (p.n_splits == 1 && (long long)p.n_kv_heads * B >= kMfmaLargeGrid)
     launch_main(ev, decode_mfma_kernel<G, HD, kMfmaWavesLarge>, grid, dim3(64 * kMfmaWavesLarge), st, p);
   else
     launch_main(ev, decode_mfma_kernel<G, HD, kMfmaWavesSmall>, grid, dim3(64 * kMfmaWavesSmall), st, p);
