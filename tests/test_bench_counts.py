@@ -111,3 +111,16 @@ def test_counter_summary_copy_calibration(tmp_path):
     assert s["FETCH_SIZE"]["scale"] == pytest.approx(2.0)
     assert s["FETCH_SIZE"]["bytes_per_dispatch"] == pytest.approx(500000.0 * 1024 * 2.0)
     assert s["WRITE_SIZE"]["bytes_per_dispatch"] == pytest.approx(100.0 * 1024 * 2.0)
+
+
+@pytest.mark.parametrize("extra", [[], ["--workload", "depthgraft_prefill_chunk"], ["--sweep"],
+                                   ["--workload", "factorized_encode_chunk"]])
+def test_bench_refuses_more_than_one_gpu(extra):
+    # every mode exits with status 2 and says why, before touching a GPU
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"] + extra,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
