@@ -506,7 +506,8 @@ def calibration_copy():
 def decode_kernel_name(wl, two_source):
     """The kernel a decode call of this workload launches for its partitions."""
     G = wl.n_q_heads // wl.n_kv_heads
-    if wl.dtype == "bf16" and wl.head_dim == 64 and not two_source and G <= 16:
+    if wl.dtype == "bf16" and not two_source and ((wl.head_dim == 64 and G <= 32)
+                                                  or (wl.head_dim == 128 and G == 16)):
         return "decode_mfma_kernel (bf16 MFMA, split-K partitions)"
     return "decode_kernel (split-K partitions)"
 
