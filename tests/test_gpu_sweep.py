@@ -28,7 +28,8 @@ def _draw(n_cases=48, seed=20261203):
         B = rng.randint(1, 3)
         if kind == "dense":
             dtype = rng.choice(["bf16", "bf16", "bf16", "f32"])
-            g = rng.choice([1, 2, 4, 8, 16] if dtype == "bf16" else [1, 2, 4, 8])
+            gs = [1, 2, 4, 8, 16] + ([32] if hd == 64 else [])
+            g = rng.choice(gs if dtype == "bf16" else [1, 2, 4, 8])
             share = rng.choice(["cla2", "cla2_top", "mid3", "identity", "depthgraft"])
             if share == "depthgraft" and g > 8:        # no two-source kernel for G > 8
                 continue
