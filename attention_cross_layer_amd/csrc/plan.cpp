@@ -177,17 +177,23 @@ extern "C" kvs_status kvs_cache_layout(const kvs_plan* plan, kvs_cache_sizes* ou
 //    G = 16): one workgroup per CU (256); with S = 1 the merge launch
 //    disappears as well;
 //  * the VALU kernel (hd 128, fp32, two sources): three workgroups per four
-//    CUs (192) when a call streams more than 384 MB, else four per CU (1024)
-//    with S <= 32: small calls are latency-bound and gain from more waves in
-//    flight (DepthGraft's 8 x 8K batch: 70 -> 60 us per single-source
-//    layer), large ones lose.  At 64K context fewer streams read HBM
-//    faster: 192 workgroups against 256, kernel alone, two alternations on
-//    one box: 154.1-155.8 vs 157.9-159.0 us at batch 4, 83.0-83.5 vs
-//    85.6-86.8 at batch 2, 302.8-303.3 vs 311.5-317.0 at batch 8 (224 and
-//    160 workgroups in between and below: 156.3-157.9, 173.0-174.0 at
-//    batch 4).
+//    CUs (192) when a call streams more than 384 MB, and for smaller calls
+//    whose (sequence, KV head) count reaches 192 to 224 workgroups with a
+//    whole number of partitions; other small calls take four per CU (1024)
+//    with S <= 32.  At 64K context fewer streams read HBM faster: 192
+//    workgroups against 256, kernel alone, two alternations on one box:
+//    154.1-155.8 vs 157.9-159.0 us at batch 4, 83.0-83.5 vs 85.6-86.8 at
+//    batch 2, 302.8-303.3 vs 311.5-317.0 at batch 8 (224 and 160 workgroups
+//    in between and below: 156.3-157.9, 173.0-174.0 at batch 4).  The same
+//    holds for 134-268 MB calls (8 KV heads, kernel alone, 192 against 1024
+//    or 32 partitions: batch x ctx 8 x 8K 45.7 vs 50.4 us, 4 x 16K 45.3 vs
+//    50.6, 2 x 32K 45.3 vs 53.6, 1 x 64K 45.4 vs 49.9, 8 x 4K 27.2 vs 29.0,
+//    1 x 32K 27.2 vs 29.4, 2 x 16K 27.4 vs 28.5); where 192 is out of reach
+//    (16 or 32 sequences: 256 workgroups at S = 2 or 1) 512 to 2048
+//    workgroups do as well or better (16 x 4K: 50.1 at 256, 50.7 at 1024).
 static const int32_t kGroupsPerCu1 = 256;
 static const int32_t kGroupsLarge = 192;
+static const int32_t kGroupsLargeMax = 224;
 static const int32_t kGroupsPerCu4 = 1024;
 static const double kSmallCallBytes = 384.0 * (1 << 20);
 
@@ -205,16 +211,17 @@ extern "C" kvs_status kvs_decode_splits(const kvs_plan* plan, int32_t batch, int
   int32_t target = kGroupsPerCu1, s_max = max_decode_splits();
   if (c.kind == KVS_DENSE && !mfma_kernel) {
     const double call_bytes = double(groups) * pages * kPage * c.head_dim * 2 * elem_bytes(c.dtype);
-    if (call_bytes <= kSmallCallBytes && G < 8) {
+    const int32_t grid_large = ((kGroupsLarge + groups - 1) / groups) * groups;
+    if (call_bytes > kSmallCallBytes || (G < 8 && grid_large <= kGroupsLargeMax)) {
+      target = kGroupsLarge;
+    } else if (G < 8) {
       target = kGroupsPerCu4;
       s_max = 32;
-    } else if (call_bytes <= kSmallCallBytes) {
+    } else {
       // groups of 8 hold one wave per SIMD: more workgroups than CUs only
       // queue (8 heads at hd 128, batch 4 x 16K: 52.0, 55.9, 65.1 us at
       // 256, 512, 1024 workgroups)
       target = kGroupsPerCu1;
-    } else {
-      target = kGroupsLarge;
     }
   }
   int32_t s = (target + groups - 1) / groups;

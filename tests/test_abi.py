@@ -152,17 +152,25 @@ def test_decode_split_choice_and_workspace():
 
 
 def test_decode_split_rule_by_kernel_and_call_size():
-    # VALU kernel (hd 128): a call streaming 1 GiB takes three workgroups per
-    # four CUs (4 x 8 x 6 = 192), one of 256 MiB four per CU (8 x 8 x 16 = 1024)
+    # VALU kernel (hd 128): three workgroups per four CUs (192) for a call
+    # streaming 1 GiB (4 x 8 x 6), and for a smaller one whose sequences and
+    # KV heads reach 192 to 224 workgroups (8 x 8 x 3 at 256 MiB, 1 x 8 x 24)
     src, w = datagen.share_map(datagen.WORKLOADS["cla2_64k"])
-    plan = K.kvs_share_plan(_cfg(32, 32, 8, 128, "bf16", 8, 65536), src, w)
+    plan = K.kvs_share_plan(_cfg(32, 32, 8, 128, "bf16", 32, 65536), src, w)
     assert K.kvs_decode_splits(plan, 4, 65536) == 6
     assert K.kvs_decode_splits(plan, 2, 65536) == 12
     assert K.kvs_decode_splits(plan, 8, 65536) == 3
-    assert K.kvs_decode_splits(plan, 8, 8192) == 16
-    # at most 32 partitions on the small-call path, at least 4 pages each
-    assert K.kvs_decode_splits(plan, 1, 65536) == 32
+    assert K.kvs_decode_splits(plan, 8, 8192) == 3
+    assert K.kvs_decode_splits(plan, 1, 65536) == 24
+    assert K.kvs_decode_splits(plan, 7, 8192) == 4     # 7 x 8 x 4 = 224
+    assert K.kvs_decode_splits(plan, 5, 8192) == 5     # 5 x 8 x 5 = 200
+    # otherwise small calls take four per CU, at most 32 partitions
+    assert K.kvs_decode_splits(plan, 16, 4096) == 8    # 16 x 8 x 2 = 256 > 224
+    assert K.kvs_decode_splits(plan, 10, 8192) == 13   # 10 x 8 x 3 = 240 > 224
+    # at least 4 pages per partition
+    assert K.kvs_decode_splits(plan, 1, 4096) == 16
     assert K.kvs_decode_splits(plan, 8, 512) == 2
+    assert K.kvs_decode_splits(plan, 32, 1024) == 4
     # a group of 8 at hd 128 runs one wave per SIMD: one workgroup per CU
     # for a small call too (4 x 8 x 8 = 256)
     plan8 = K.kvs_share_plan(_cfg(32, 64, 8, 128, "bf16", 8, 65536), src, w)
