@@ -199,10 +199,12 @@ KVS_API kvs_status kvs_cache_layout(const kvs_plan* plan, kvs_cache_sizes* out);
  * is passed to kvs_attn_decode: chosen from batch, KV heads, the longest
  * sequence and the plan's decode kernel so the launch fills the GPU (one
  * workgroup per CU for the factorized and MFMA kernels; for the dot-product
- * kernel three per four CUs on calls streaming more than 384 MB, four per
- * CU on smaller ones, one per CU for groups of 8 heads); at least 4 pages
- * per partition, at most 64 partitions; partition boundaries fall on 64-key
- * page boundaries. */
+ * kernel three per four CUs (192) on calls streaming more than 384 MB and on
+ * smaller calls whose (sequence, KV head) pairs reach 192 to 224 workgroups
+ * with a whole number of partitions, otherwise four per CU (at most 32
+ * partitions) on smaller calls, one per CU for groups of 8 heads); at least
+ * 4 pages per partition, at most 64 partitions; partition boundaries fall
+ * on 64-key page boundaries. */
 KVS_API kvs_status kvs_decode_splits(const kvs_plan* plan, int32_t batch,
                                      int32_t max_seq_len, int32_t* n_splits);
 /* Workspace bytes kvs_attn_decode needs for (batch, n_splits), n_splits in
