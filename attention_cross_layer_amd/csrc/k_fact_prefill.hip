@@ -1,5 +1,6 @@
 // Causal (or full) prefill-chunk attention over the factorized cache, in the
-// 48-wide coefficient space, on bf16 MFMA with fp32 accumulation.
+// 48-wide coefficient space, on MFMA with fp32 accumulation (fp16 operands
+// for the scores, bf16 for the values).
 //
 // Keys and values follow DepthWeave-KV ("DepthWeave-KV: Smarter KV Cache
 // Compression by Sharing Across Layers and Adapting Per Token", Core
@@ -12,15 +13,14 @@
 // (query, key) pair contracting 48 coefficients on each side instead of
 // head_dim, and the bases entering once per query row at both ends.
 //
-// Decomposition (v_mfma_f32_32x32x16_bf16: lane l of A/B holds row or column
+// Decomposition (v_mfma_f32_32x32x16_f16 / _bf16: lane l of A/B holds row or column
 // l%32 and k = 8(l/32)+e; result register r of lane l is row
 // 8(r/4) + 4(l/32) + r%4, column l%32):
 //   workgroup = 4 waves on one KV head, each owning 32 query rows of one head
 //   (min(G, 4) heads x 4/min(G, 4) blocks of 32 positions), as the dense
 //   prefill.
 //   prologue  Q~^T = B^K Q^T and U~^T = [U^K; 0] Q^T (2 hd/16 MFMAs), each
-//             split into a bf16 high part and the bf16 rounding of the
-//             remainder.  Their result registers serve as B operands
+//             rounded to fp16.  Their result registers serve as B operands
 //             unchanged: register r holds
 //             coefficient 8(r/4) + 4(l/32) + r%4, so in every product over the
 //             coefficient space the k index visits coefficients in that order.
@@ -29,13 +29,16 @@
 //             16-byte LDS read.
 //   per 64-key page, double-buffered in LDS, the next page's global loads in
 //   registers (its meta entries one further page ahead):
-//     staging  C^K [64 keys][32], S^K = s^K d^K [64][16] (codes taken from
-//              their rank-packed granules, scaled in fp32, rounded to bf16),
-//              C^V^T [32][64 keys], S^V^T = (s^V d^V)^T [16][64 keys]; keys
+//     staging  C^K [64 keys][32] (converted to fp16: exact for magnitudes
+//              up to 65504), S^K = s^K d^K [64][16] (codes taken from their
+//              rank-packed granules, scaled in fp32, rounded to fp16),
+//              C^V^T [32][64 keys], S^V^T = (s^V d^V)^T [16][64 keys] (bf16,
+//              the scaled codes rounded to bf16); keys
 //              past the sequence end, or on a corrupt page-table entry, are
 //              zero on the value side and have no codes.
-//     S^T = C^K Q~^T + S^K U~^T   12 MFMAs per wave (high parts and
-//              remainders)
+//     S^T = C^K Q~^T + S^K U~^T   6 fp16 MFMAs per wave (bf16 operands
+//              would need a high part and a remainder of Q~, U~ each, twice
+//              the products, for the same accuracy)
 //     softmax  online per query row, as the dense prefill
 //     A^T += C^V^T P^T, D^T += S^V^T P^T   8 MFMAs (rows 16..31 of the second
 //              product's A operand are zero)
@@ -54,6 +57,8 @@ namespace kvs {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
@@ -110,6 +115,24 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x1
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+__device__ __forceinline__ f32x16_t mfma32h(const uint4& a, const uint4& b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+
+// two floats -> packed fp16 pair, round to nearest even
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// eight bf16 values -> eight fp16 values (exact for magnitudes in
+// [2^-14, 65504]; smaller ones keep fp16's subnormal precision)
+__device__ __forceinline__ uint4 bf16x8_to_f16(const uint4& x) {
+  auto cv = [](uint32_t w) { return pack_f16(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)); };
+  return make_uint4(cv(x.x), cv(x.y), cv(x.z), cv(x.w));
+}
+
 // two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
@@ -133,6 +156,18 @@ __device__ __forceinline__ void split8(const f32x16_t& x, int r0, uint4& hi, uin
   }
   hi = make_uint4(pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]), pack_bf16(h[6], h[7]));
   lo = make_uint4(pack_bf16(l[0], l[1]), pack_bf16(l[2], l[3]), pack_bf16(l[4], l[5]), pack_bf16(l[6], l[7]));
+}
+
+// four int8 codes (the bytes of w) times s, as four fp16 values
+__device__ __forceinline__ uint2 scaled_codes_f16(uint32_t w, float s) {
+  return make_uint2(pack_f16(s * (float)(int8_t)(w & 0xffu), s * (float)(int8_t)((w >> 8) & 0xffu)),
+                    pack_f16(s * (float)(int8_t)((w >> 16) & 0xffu), s * (float)(int8_t)(w >> 24)));
+}
+
+// eight accumulator registers as fp16 (round to nearest even)
+__device__ __forceinline__ uint4 to_f16x8(const f32x16_t& x, int r0) {
+  return make_uint4(pack_f16(x[r0], x[r0 + 1]), pack_f16(x[r0 + 2], x[r0 + 3]), pack_f16(x[r0 + 4], x[r0 + 5]),
+                    pack_f16(x[r0 + 6], x[r0 + 7]));
 }
 
 // four int8 codes (the bytes of w) times s, as four bf16 values
@@ -242,15 +277,16 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
       const int p0 = swz16(8 * cc), p1 = swz16(8 * cc + 4);
       uint16_t* rowp = base + tk * kR;
       const int sw = (tk >> 2) & 3;
-      *reinterpret_cast<uint2*>(rowp + (((p0 >> 3) ^ sw) << 3) + (p0 & 7)) = make_uint2(ck_r.x, ck_r.y);
-      *reinterpret_cast<uint2*>(rowp + (((p1 >> 3) ^ sw) << 3) + (p1 & 7)) = make_uint2(ck_r.z, ck_r.w);
+      const uint4 ch = bf16x8_to_f16(ck_r);
+      *reinterpret_cast<uint2*>(rowp + (((p0 >> 3) ^ sw) << 3) + (p0 & 7)) = make_uint2(ch.x, ch.y);
+      *reinterpret_cast<uint2*>(rowp + (((p1 >> 3) ^ sw) << 3) + (p1 & 7)) = make_uint2(ch.z, ch.w);
     }
     // S^K: codes 4cq..4cq+3 of key skey, times its scale
     {
       const float s = half_bits_to_float(sk_r);
       const int p = swz16(4 * cq);
       uint16_t* rowp = base + kCK + skey * kRM;
-      *reinterpret_cast<uint2*>(rowp + (((p >> 3) ^ ((skey >> 3) & 1)) << 3) + (p & 7)) = scaled_codes(dk_r, s);
+      *reinterpret_cast<uint2*>(rowp + (((p >> 3) ^ ((skey >> 3) & 1)) << 3) + (p & 7)) = scaled_codes_f16(dk_r, s);
     }
     // C^V^T: chunk tid of the cV page = coefficients ia and ia + 4 of tokens
     // 4tq..4tq+3; absent keys zero
@@ -299,10 +335,10 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
   }
   uint32_t meta_next = load_meta(1, ph_a);
 
-  // Q~ and U~ as bf16 high parts and bf16 remainders: rounding them alone
+  // Q~ and U~ as fp16 (11 significant bits): rounded to bf16 (8 bits) they
   // moved scores enough to take single outputs past 1e-2 where a few keys
   // dominate a row
-  uint4 bq[2], bu, bq_lo[2], bu_lo;
+  uint4 bq[2], bu;
   {
     const int qrow = row_ok ? row : (n - 1);
     const uint16_t* qp = a.q + (((size_t)b * n + qrow) * a.n_q_heads + head) * HD;
@@ -319,8 +355,8 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
       qu = mfma32(au, qv, qu);
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) split8(qt, 8 * ks, bq[ks], bq_lo[ks]);
-    split8(qu, 0, bu, bu_lo);
+    for (int ks = 0; ks < 2; ++ks) bq[ks] = to_f16x8(qt, 8 * ks);
+    bu = to_f16x8(qu, 0);
   }
 
   f32x16_t acc_c = f32x16_t{}, acc_d = f32x16_t{};
@@ -354,12 +390,9 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
       const uint4 c0 = *reinterpret_cast<const uint4*>(rowp + (((0 + hh) ^ sw) << 3));
       const uint4 c1 = *reinterpret_cast<const uint4*>(rowp + (((2 + hh) ^ sw) << 3));
       const uint4 dq = *reinterpret_cast<const uint4*>(base + kCK + key * kRM + ((hh ^ ((key >> 3) & 1)) << 3));
-      s[kb] = mfma32(c0, bq[0], f32x16_t{});
-      s[kb] = mfma32(c1, bq[1], s[kb]);
-      s[kb] = mfma32(dq, bu, s[kb]);
-      s[kb] = mfma32(c0, bq_lo[0], s[kb]);
-      s[kb] = mfma32(c1, bq_lo[1], s[kb]);
-      s[kb] = mfma32(dq, bu_lo, s[kb]);
+      s[kb] = mfma32h(c0, bq[0], f32x16_t{});
+      s[kb] = mfma32h(c1, bq[1], s[kb]);
+      s[kb] = mfma32h(dq, bu, s[kb]);
     }
 
     // ---- online softmax for this lane's query row on raw scores

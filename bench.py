@@ -553,13 +553,13 @@ def issue_roofline(wl, fact, us):
     softmax's VALU work per pair at the fp32 vector rate plus the MFMA work
     per pair as the kernel issues it, the two not overlapped (per-SIMD issue
     counters show them serialised).  MFMA FLOPs issued per pair: dense
-    4*hd (two products); factorized 2*(2*R + 2*Rmax) for the scores (q~, u~
-    as bf16 high and low parts) + 2*(R + 2*Rmax) for the values (the
+    4*hd (two products); factorized 2*(R + Rmax) for the scores (q~, u~ as
+    fp16, one product) + 2*(R + 2*Rmax) for the values (the
     residual product runs 32 rows wide, half of them zero)."""
     n, T = wl.prefill_n, wl.ctx
     pairs = wl.n_q_heads * (n * (T - n) + n * (n + 1) // 2)
     R, Rm = wl.basis_rank, wl.resid_rank_max
-    mfma_flops = (2 * (2 * R + 2 * Rm) + 2 * (R + 2 * Rm)) if fact else 4 * wl.head_dim
+    mfma_flops = (2 * (R + Rm) + 2 * (R + 2 * Rm)) if fact else 4 * wl.head_dim
     valu_s = VALU_SLOTS_PER_PAIR / (FP32_VECTOR_PEAK_TFLOPS * 1e12 / 2)
     mfma_s = mfma_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
     peak = 1.0 / (valu_s + mfma_s)
@@ -620,7 +620,7 @@ def prefill_main(args, workload):
             K.kvs_append_factorized(plan, cache, l, ck, cv, dk, dv, sk, sv, r_chunk, start,
                                     stream=stream)
         flops = fact_prefill_flops(n, T, wl.n_q_heads, wl.head_dim, wl.basis_rank + wl.resid_rank_max)
-        kernel = "fact_prefill_kernel (bf16 MFMA in the coefficient space, causal)"
+        kernel = "fact_prefill_kernel (fp16 score / bf16 value MFMA in the coefficient space, causal)"
     else:
         src, w, plan, cache, owners = setup(wl)
         layers = owners

@@ -421,9 +421,11 @@ KVS_API kvs_status kvs_attn_decode_noalloc(const kvs_plan* plan, const kvs_cache
  * Dense bf16 plans, and factorized plans (head_dim 64/128, ranks 32/16),
  * which attend in the coefficient space: q~ = B^K q and u~ = U^K q once per
  * query, scores c_t . q~ + s_t (d_t . u~), value accumulators in the 48
- * coefficients mapped back through B^V and U^V once per query row; q~ and u~
- * enter the MFMA as a bf16 high part plus the bf16 remainder, the scaled
- * codes s_t d_t as bf16.  Other plans ->
+ * coefficients mapped back through B^V and U^V once per query row; the score
+ * products take fp16 operands (q~, u~ and the scaled codes s_t d_t rounded
+ * to fp16, the coefficients c_t converted exactly: their magnitudes must stay
+ * below 65504), the value products bf16 (probabilities, c^V_t, and
+ * s^V_t d^V_t rounded to bf16).  Other plans ->
  * KVS_ERR_UNSUPPORTED. */
 KVS_API kvs_status kvs_attn_prefill_chunk(const kvs_plan* plan, const kvs_cache* cache,
                                           int32_t layer, const void* q, int32_t n,

@@ -85,6 +85,18 @@ def test_issue_roofline_peak():
     assert got["achieved"] == pytest.approx(pairs / 1e-3, rel=1e-12)
 
 
+def test_issue_roofline_peak_factorized():
+    # factorized: per 64-key page a wave of 32 query rows issues 6 score
+    # products (2 key blocks x 3 steps over the 48 coefficients) and 8 value
+    # products (2 column blocks x 4 key steps), each a 32 x 32 x 16 MFMA
+    wl = bench.prefill_wl("factorized_prefill_chunk")
+    flops_per_pair = (6 + 8) * 2 * 32 * 32 * 16 / (32 * 64)
+    got = bench.issue_roofline(wl, True, 1000.0)
+    assert got["mfma_flops_per_pair_issued"] == flops_per_pair
+    per_pair_s = 6.5 / (157.3e12 / 2) + flops_per_pair / 2.5e15
+    assert got["peak"] == pytest.approx(1.0 / per_pair_s, rel=1e-12)
+
+
 def _write_csv(path, header, rows):
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w", newline="") as f:
