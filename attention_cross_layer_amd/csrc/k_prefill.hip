@@ -9,9 +9,9 @@
 // reusing layers read the source layer's K/V).  A two-source layer reads the
 // DepthGraft mix K~ = w0 K_s0 + w1 K_s1 ("DepthGraft: Structural
 // Regularization through Hierarchical Cross-Layer KV Reconstruction",
-// Abstract), formed in fp32 while a tile is staged and carried into the
-// MFMA as two bf16 tiles, the rounded mix and the rounding of its remainder
-// (about 16 significant bits), so both products run twice for such a layer.
+// Abstract), formed in fp32 while a tile is staged and rounded to fp16 (11
+// significant bits); such a layer's products run on the fp16 MFMA, with its
+// queries (bf16, converted exactly) and probabilities in fp16 as well.
 // DepthGraft's owner layers are the only ones that need prefill for all
 // prompt tokens (the Abstract's "prefill early completion").
 //
@@ -95,6 +95,24 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x1
 }
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+
+__device__ __forceinline__ f32x16_t mfma32h(const uint4& a, const uint4& b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+
+// two floats -> packed fp16 pair, round to nearest even
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  const f16x2_t v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// a.lo*b.lo + a.hi*b.hi + c for two fp16 pairs (v_dot2_f32_f16)
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
 
 // two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -103,10 +121,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 }
 
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;   // (1.0, 1.0) in bf16
+constexpr uint32_t kOnesF16x2 = 0x3C003C00u;    // (1.0, 1.0) in fp16
 constexpr float kBumpLog2 = 8.f;                // lazy-maximum slack (log2 units)
 
-// w0*a + w1*b per bf16 element of two 16-byte chunks, rounded back to bf16.
-__device__ __forceinline__ uint4 mix_chunk(const uint4& a, const uint4& b, float w0, float w1) {
+// w0*a + w1*b per bf16 element of two 16-byte chunks, formed in fp32 and
+// rounded to fp16 (11 significant bits against bf16's 8).
+__device__ __forceinline__ uint4 mix_chunk_f16(const uint4& a, const uint4& b, float w0, float w1) {
   uint4 r;
   const uint32_t* pa = &a.x;
   const uint32_t* pb = &b.x;
@@ -115,26 +135,26 @@ __device__ __forceinline__ uint4 mix_chunk(const uint4& a, const uint4& b, float
   for (int i = 0; i < 4; ++i) {
     const float lo = fmaf(w0, dev::bf16_lo(pa[i]), w1 * dev::bf16_lo(pb[i]));
     const float hi = fmaf(w0, dev::bf16_hi(pa[i]), w1 * dev::bf16_hi(pb[i]));
-    pr[i] = pack_bf16(lo, hi);
+    pr[i] = pack_f16(lo, hi);
   }
   return r;
 }
 
-// The bf16 remainder w0*a + w1*b - bf16(w0*a + w1*b) per element of two
-// 16-byte chunks (the mix in fp32, as mix_chunk forms it).
-__device__ __forceinline__ uint4 mix_chunk_rest(const uint4& a, const uint4& b, float w0, float w1) {
-  uint4 r;
-  const uint32_t* pa = &a.x;
-  const uint32_t* pb = &b.x;
-  uint32_t* pr = &r.x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = fmaf(w0, dev::bf16_lo(pa[i]), w1 * dev::bf16_lo(pb[i]));
-    const float hi = fmaf(w0, dev::bf16_hi(pa[i]), w1 * dev::bf16_hi(pb[i]));
-    const uint32_t h = pack_bf16(lo, hi);
-    pr[i] = pack_bf16(lo - dev::bf16_lo(h), hi - dev::bf16_hi(h));
-  }
-  return r;
+// eight bf16 values -> eight fp16 values (exact for magnitudes in
+// [2^-14, 65504]; smaller ones keep fp16's subnormal precision)
+__device__ __forceinline__ uint4 bf16x8_to_f16(const uint4& x) {
+  auto cv = [](uint32_t w) { return pack_f16(dev::bf16_lo(w), dev::bf16_hi(w)); };
+  return make_uint4(cv(x.x), cv(x.y), cv(x.z), cv(x.w));
+}
+
+// One MFMA of the kernel: bf16 operands for one-source layers, fp16 for
+// two-source layers (whose tiles are the fp16 mix).
+template <int NSRC>
+__device__ __forceinline__ f32x16_t mfma_op(const uint4& a, const uint4& b, f32x16_t c) {
+  if constexpr (NSRC == 2)
+    return mfma32h(a, b, c);
+  else
+    return mfma32(a, b, c);
 }
 
 // Waves per workgroup.  Eight waves sharing each staged tile halve the
@@ -158,13 +178,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][64 * HD];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][HD * kVRow];
-  // Two sources: the bf16 remainders of the mixed K and V^T tiles, so that
-  // both products see the fp32 mix to about 16 bits.  Rounding the mixed
-  // tiles to bf16 alone moved single outputs by up to 1e-2 where a few keys
-  // dominate a row (mostly through the scores), at the edge of the error
-  // bound; the remainders double the MFMAs of a two-source layer.
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds_lo[NSRC == 2 ? 2 : 1][NSRC == 2 ? 64 * HD : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds_lo[NSRC == 2 ? 2 : 1][NSRC == 2 ? HD * kVRow : 8];
+  // Two sources: the tiles hold the fp32 mix rounded to fp16, and the
+  // queries and probabilities enter those products as fp16 too.  Rounding
+  // the mixed tiles to bf16 moved single outputs by up to 1e-2 where a few
+  // keys dominate a row (mostly through the scores), at the edge of the
+  // error bound; fp16 keeps 3 more bits in one product per step.
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -205,8 +223,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
     const int qrow = row_ok ? row : (n - 1);                 // stay in bounds
     const uint16_t* qp = a.q + (((size_t)b * n + qrow) * a.n_q_heads + head) * HD;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
+    for (int ks = 0; ks < KS; ++ks) {
       qreg[ks] = *reinterpret_cast<const uint4*>(qp + (2 * ks + hh) * 8);
+      if constexpr (NSRC == 2) qreg[ks] = bf16x8_to_f16(qreg[ks]);
+    }
   }
 
   const int32_t* pt = a.page_table + (size_t)b * a.pages_per_seq;
@@ -248,11 +268,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
       constexpr int NCW = NCH / kWays, KPP = 64 / kWays;   // chunks per lane, keys per pass
       const int j = qi / (NCW * 64), cc = (qi / 64) % NCW, kk = (qi % 64) / kWays, w = qi % kWays;
       const int key = KPP * j + kk, c = kWays * cc + w;
-      uint4 v = NSRC == 2 ? mix_chunk(st.k[0][u], st.k[NSRC - 1][u], a.w0, a.w1) : st.k[0][u];
+      uint4 v = NSRC == 2 ? mix_chunk_f16(st.k[0][u], st.k[NSRC - 1][u], a.w0, a.w1) : st.k[0][u];
       *reinterpret_cast<uint4*>(&k_lds[buf][key * HD + ((c ^ (key & (NCH - 1))) * 8)]) = v;
-      if constexpr (NSRC == 2)
-        *reinterpret_cast<uint4*>(&k_lds_lo[buf][key * HD + ((c ^ (key & (NCH - 1))) * 8)]) =
-            mix_chunk_rest(st.k[0][u], st.k[1][u], a.w0, a.w1);
     }
     // V^T: this thread holds VCH consecutive key pairs of its 4 dims (a
     // dword = one dim of a key pair), so each dim row takes one VCH-dword
@@ -262,7 +279,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
       uint32_t w[4][VCH];
 #pragma unroll
       for (int u = 0; u < VCH; ++u) {
-        const uint4 v = NSRC == 2 ? mix_chunk(st.v[0][u], st.v[NSRC - 1][u], a.w0, a.w1) : st.v[0][u];
+        const uint4 v = NSRC == 2 ? mix_chunk_f16(st.v[0][u], st.v[NSRC - 1][u], a.w0, a.w1) : st.v[0][u];
         w[0][u] = v.x;
         w[1][u] = v.y;
         w[2][u] = v.z;
@@ -286,33 +303,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
         const int k0 = 2 * VCH * q;                          // first of this thread's keys
 #pragma unroll
         for (int u = 0; u < VCH; ++u) row[swz16(k0 + 2 * u) / 2] = w[i][u];
-      }
-      if constexpr (NSRC == 2) {
-        // the remainders, stored after the rounded mix to keep registers down
-#pragma unroll
-        for (int u = 0; u < VCH; ++u) {
-          const uint4 v = mix_chunk_rest(st.v[0][u], st.v[1][u], a.w0, a.w1);
-          w[0][u] = v.x;
-          w[1][u] = v.y;
-          w[2][u] = v.z;
-          w[3][u] = v.w;
-        }
-        if (!(page_ok && key0 + 64 <= T)) {
-#pragma unroll
-          for (int u = 0; u < VCH; ++u) {
-            const int k0 = key0 + 2 * (q * VCH + u);
-            const uint32_t mk = (page_ok && k0 < T ? 0x0000ffffu : 0u) | (page_ok && k0 + 1 < T ? 0xffff0000u : 0u);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) w[i][u] &= mk;
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t* row = reinterpret_cast<uint32_t*>(&v_lds_lo[buf][0] + vrow_of(4 * L + i) * kVRow);
-          const int k0 = 2 * VCH * q;
-#pragma unroll
-          for (int u = 0; u < VCH; ++u) row[swz16(k0 + 2 * u) / 2] = w[i][u];
-        }
       }
     }
   };
@@ -347,16 +337,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
       for (int ks = 0; ks < KS; ++ks) {
         const int c = 2 * ks + hh;
         const uint4 kv = *reinterpret_cast<const uint4*>(&k_lds[buf][key * HD + ((c ^ (key & (NCH - 1))) * 8)]);
-        s[kb] = mfma32(kv, qreg[ks], s[kb]);
-        if constexpr (NSRC == 2) {
-          const uint4 kl = *reinterpret_cast<const uint4*>(&k_lds_lo[buf][key * HD + ((c ^ (key & (NCH - 1))) * 8)]);
-          s[kb] = mfma32(kl, qreg[ks], s[kb]);
-        }
+        s[kb] = mfma_op<NSRC>(kv, qreg[ks], s[kb]);
       }
     }
     // the K operand reads run four ahead of the MFMAs that take them (two
     // ahead with two sources, whose tile stages hold twice the registers)
-    constexpr int NQK = 2 * KS * NSRC;        // score MFMAs (and K reads) per tile
+    constexpr int NQK = 2 * KS;               // score MFMAs (and K reads) per tile
     constexpr int AHEAD = NSRC == 2 ? 2 : 4;
     __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
 #pragma unroll
@@ -406,15 +392,27 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
 #pragma unroll
         for (int e = 0; e < 8; ++e) p[e] = dev::fast_exp2(fmaf(s[kb][8 * sh + e], a.scale_log2, neg));
         uint4 w;
-        w.x = pack_bf16(p[0], p[1]);
-        w.y = pack_bf16(p[2], p[3]);
-        w.z = pack_bf16(p[4], p[5]);
-        w.w = pack_bf16(p[6], p[7]);
-        // the running sum adds the same bf16-rounded probabilities (dot with ones)
-        lt = dev::dot2_bf16(w.x, kOnesBf16x2, lt);
-        lt = dev::dot2_bf16(w.y, kOnesBf16x2, lt);
-        lt = dev::dot2_bf16(w.z, kOnesBf16x2, lt);
-        lt = dev::dot2_bf16(w.w, kOnesBf16x2, lt);
+        if constexpr (NSRC == 2) {
+          // p <= 2^kBumpLog2: in fp16 range
+          w.x = pack_f16(p[0], p[1]);
+          w.y = pack_f16(p[2], p[3]);
+          w.z = pack_f16(p[4], p[5]);
+          w.w = pack_f16(p[6], p[7]);
+          lt = dot2_f16(w.x, kOnesF16x2, lt);
+          lt = dot2_f16(w.y, kOnesF16x2, lt);
+          lt = dot2_f16(w.z, kOnesF16x2, lt);
+          lt = dot2_f16(w.w, kOnesF16x2, lt);
+        } else {
+          w.x = pack_bf16(p[0], p[1]);
+          w.y = pack_bf16(p[2], p[3]);
+          w.z = pack_bf16(p[4], p[5]);
+          w.w = pack_bf16(p[6], p[7]);
+          // the running sum adds the same rounded probabilities (dot with ones)
+          lt = dev::dot2_bf16(w.x, kOnesBf16x2, lt);
+          lt = dev::dot2_bf16(w.y, kOnesBf16x2, lt);
+          lt = dev::dot2_bf16(w.z, kOnesBf16x2, lt);
+          lt = dev::dot2_bf16(w.w, kOnesBf16x2, lt);
+        }
         pb[2 * kb + sh] = w;
       }
     l_run = fmaf(l_run, alpha, lt);
@@ -432,11 +430,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void prefill_kernel(PrefillParams a
       for (int mb = 0; mb < MB; ++mb) {
         const int d = 32 * mb + col;
         const uint16_t* vrow = &v_lds[buf][vrow_of(d) * kVRow + 16 * sp + 8 * hh];
-        o[mb] = mfma32(*reinterpret_cast<const uint4*>(vrow), pb[sp], o[mb]);
-        if constexpr (NSRC == 2) {
-          const uint16_t* vlo = &v_lds_lo[buf][vrow_of(d) * kVRow + 16 * sp + 8 * hh];
-          o[mb] = mfma32(*reinterpret_cast<const uint4*>(vlo), pb[sp], o[mb]);
-        }
+        o[mb] = mfma_op<NSRC>(*reinterpret_cast<const uint4*>(vrow), pb[sp], o[mb]);
       }
   };
   for (int t = 0; t < n_tiles; t += 2) {

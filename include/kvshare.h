@@ -410,10 +410,11 @@ KVS_API kvs_status kvs_attn_decode_noalloc(const kvs_plan* plan, const kvs_cache
  * layers of a DepthGraft map need the whole prompt ("DepthGraft: Structural
  * Regularization through Hierarchical Cross-Layer KV Reconstruction",
  * Abstract: prefill completes early).  Keys of a page whose page-table entry
- * lies outside [0, n_phys_pages) get no weight, as in the decode.  Query and key tiles go through bf16
- * MFMA with fp32 accumulation; a two-source layer's mixed K~/V~ tiles (mixed
- * in fp32) enter the MFMA as their bf16 rounding plus the bf16 rounding of
- * the remainder.
+ * lies outside [0, n_phys_pages) get no weight, as in the decode.  Query and
+ * key tiles go through bf16 MFMA with fp32 accumulation; a two-source
+ * layer's mixed K~/V~ tiles (mixed in fp32) are rounded to fp16 and its
+ * products run on fp16 operands (queries converted from bf16 exactly,
+ * probabilities in fp16), which needs |q|, |K~|, |V~| below 65504.
  *   q        device bf16 [batch][n][Hq][hd]
  *   seq_len  device int32 [batch], each >= n; a row whose position P is
  *            below 0 (seq_len[b] < n) sees no key and yields zeros
