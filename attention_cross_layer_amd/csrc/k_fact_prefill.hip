@@ -27,8 +27,8 @@
 //             Staged tiles store each 16-wide group with its quads 1 and 2
 //             swapped (swz16), which puts a lane's 8 operand values in one
 //             16-byte LDS read.
-//   per 64-key page, double-buffered in LDS, the next page's global loads in
-//   registers (its meta entries one further page ahead):
+//   per 64-key page, double-buffered in LDS, the global loads of the next two
+//   pages in two register stages (their meta entries one page further ahead):
 //     staging  C^K [64 keys][32] (converted to fp16: exact for magnitudes
 //              up to 65504), S^K = s^K d^K [64][16] (codes taken from their
 //              rank-packed granules, scaled in fp32, rounded to fp16),
@@ -230,7 +230,10 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
   const auto r_sk = rsrc(a.sk, P * H * (kPage * 2));
   const auto r_sv = rsrc(a.sv, P * H * (kPage * 2));
   const auto r_meta = rsrc(a.meta, P * (kPage * 2));
-  const int32_t* pt = a.page_table + (size_t)b * a.pages_per_seq;
+  // page-table entries through the constant address space: scalar loads,
+  // whose waits leave the vector loads of the staged pages in flight
+  typedef const __attribute__((address_space(4))) int32_t const_i32;
+  const_i32* pt = (const_i32*)(a.page_table + (size_t)b * a.pages_per_seq);
 
   // staging roles of this thread: 16-byte chunk `tid` of the cK and cV pages;
   // codes 4cq..4cq+3 and the scales of key skey
@@ -246,47 +249,50 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
     return ld2(r_meta, on ? ((uint32_t)ph * kPage + skey) * 2 : kOOB);
   };
 
-  uint4 ck_r, cv_r;
-  uint32_t dk_r, dv_r, sk_r, sv_r;
-  int ph_r;
-  auto load_tile = [&](int t, int ph, uint32_t meta) {
-    ph_r = ph;
+  // one page's global loads, held in registers until the page is staged
+  struct Stage {
+    uint4 ck, cv;
+    uint32_t dk, dv, sk, sv;
+    int ph;
+  };
+  auto load_tile = [&](int t, int ph, uint32_t meta, Stage& st) {
+    st.ph = ph;
     const uint32_t page_kv = (uint32_t)ph * H + kvh;
     const uint32_t cb = ph >= 0 ? page_kv * (kPage * kR * 2) + tid * 16 : kOOB;
-    ck_r = ld16(r_ck, cb);
-    cv_r = ld16(r_cv, cb);
+    st.ck = ld16(r_ck, cb);
+    st.cv = ld16(r_cv, cb);
     // meta is zero for absent keys: rank 0, no granule
     const int rank = min((int)(meta & 0xffu), kRM);
     const uint32_t g = min(meta >> 8, (uint32_t)(kGranules - 2)) + (cq >> 1);
     const uint32_t co = 8 * (cq >> 1) < rank ? page_kv * (kGranules * 8) + g * 8 + 4 * (cq & 1) : kOOB;
-    dk_r = ld4(r_dk, co);
-    dv_r = ld4(r_dv, co);
+    st.dk = ld4(r_dk, co);
+    st.dv = ld4(r_dv, co);
     // scales of absent keys (unwritten memory) stay zero: a NaN pattern
     // times a zero code would not
     const uint32_t so = ph >= 0 && t * 64 + skey < T ? (page_kv * kPage + skey) * 2 : kOOB;
-    sk_r = ld2(r_sk, so);
-    sv_r = ld2(r_sv, so);
+    st.sk = ld2(r_sk, so);
+    st.sv = ld2(r_sv, so);
   };
-  auto store_tile = [&](int t, int buf) {
+  auto store_tile = [&](int t, int buf, const Stage& st) {
     uint16_t* base = lds + buf * kTile;
     const int key0 = t * 64;
-    const bool page_ok = ph_r >= 0;
+    const bool page_ok = st.ph >= 0;
     // C^K: chunk tid of the cK page = coefficients 8cc..8cc+7 of token tk
     {
       const int cc = tid >> 6, tk = tid & 63;
       const int p0 = swz16(8 * cc), p1 = swz16(8 * cc + 4);
       uint16_t* rowp = base + tk * kR;
       const int sw = (tk >> 2) & 3;
-      const uint4 ch = bf16x8_to_f16(ck_r);
+      const uint4 ch = bf16x8_to_f16(st.ck);
       *reinterpret_cast<uint2*>(rowp + (((p0 >> 3) ^ sw) << 3) + (p0 & 7)) = make_uint2(ch.x, ch.y);
       *reinterpret_cast<uint2*>(rowp + (((p1 >> 3) ^ sw) << 3) + (p1 & 7)) = make_uint2(ch.z, ch.w);
     }
     // S^K: codes 4cq..4cq+3 of key skey, times its scale
     {
-      const float s = half_bits_to_float(sk_r);
+      const float s = half_bits_to_float(st.sk);
       const int p = swz16(4 * cq);
       uint16_t* rowp = base + kCK + skey * kRM;
-      *reinterpret_cast<uint2*>(rowp + (((p >> 3) ^ ((skey >> 3) & 1)) << 3) + (p & 7)) = scaled_codes_f16(dk_r, s);
+      *reinterpret_cast<uint2*>(rowp + (((p >> 3) ^ ((skey >> 3) & 1)) << 3) + (p & 7)) = scaled_codes_f16(st.dk, s);
     }
     // C^V^T: chunk tid of the cV page = coefficients ia and ia + 4 of tokens
     // 4tq..4tq+3; absent keys zero
@@ -303,13 +309,13 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
       }
       uint16_t* cvt = base + kCK + kSK;
       const int p = swz16(4 * tq);
-      *reinterpret_cast<uint2*>(cvt + ia * kVRow + p) = make_uint2(cv_r.x & m0, cv_r.y & m1);
-      *reinterpret_cast<uint2*>(cvt + (ia + 4) * kVRow + p) = make_uint2(cv_r.z & m0, cv_r.w & m1);
+      *reinterpret_cast<uint2*>(cvt + ia * kVRow + p) = make_uint2(st.cv.x & m0, st.cv.y & m1);
+      *reinterpret_cast<uint2*>(cvt + (ia + 4) * kVRow + p) = make_uint2(st.cv.z & m0, st.cv.w & m1);
     }
     // S^V^T: codes 4cq..4cq+3 of key skey (zero codes for absent keys)
     {
-      const float s = half_bits_to_float(sv_r);
-      const uint2 w = scaled_codes(dv_r, s);
+      const float s = half_bits_to_float(st.sv);
+      const uint2 w = scaled_codes(st.dv, s);
       uint16_t* svt = base + kCK + kSK + kCV + swz16(skey);
       svt[(4 * cq + 0) * kVRow] = (uint16_t)(w.x & 0xffffu);
       svt[(4 * cq + 1) * kVRow] = (uint16_t)(w.x >> 16);
@@ -326,14 +332,22 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
         r == 0 ? (uint16_t)0x3F80u : (uint16_t)0u;
   }
 
-  // ---- first page's requests, then the query contraction with the bases.
-  // Physical pages are looked up a tile before the loads that need them.
-  int ph_a = phys_of(1), ph_b = phys_of(2);   // tiles t + 1 and t + 2 of the loop
+  // ---- the first two pages' requests, then the query contraction with the
+  // bases.  Two register stages: a page's loads are issued two tiles before
+  // it is staged, its meta entries (which the code addresses need) one tile
+  // before that.
+  Stage sa, sb;
+  int ph_2, ph_3;                       // pages of the loop's tiles t + 2, t + 3
+  uint32_t meta_2;                      // meta entries of tile t + 2
   {
-    const int ph0 = phys_of(0);
-    load_tile(0, ph0, load_meta(0, ph0));
+    const int ph0 = phys_of(0), ph1 = phys_of(1);
+    const uint32_t m0 = load_meta(0, ph0), m1 = load_meta(1, ph1);
+    ph_2 = phys_of(2);
+    meta_2 = load_meta(2, ph_2);
+    ph_3 = phys_of(3);
+    load_tile(0, ph0, m0, sa);
+    load_tile(1, ph1, m1, sb);
   }
-  uint32_t meta_next = load_meta(1, ph_a);
 
   // Q~ and U~ as fp16 (11 significant bits): rounded to bf16 (8 bits) they
   // moved scores enough to take single outputs past 1e-2 where a few keys
@@ -363,20 +377,19 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
   float m_run = -INFINITY;
   const float bump_gap = kBumpLog2 / a.scale_log2;   // in raw score units
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    const int ph_c = phys_of(t + 3);
+  auto tile_step = [&](int t, int buf, Stage& st) {
+    // meta entries of tile t + 3 first: loads complete in order, so waiting
+    // for them one tile later does not wait for the page loads issued below
+    const uint32_t meta_3 = load_meta(t + 3, ph_3);
+    const int ph_4 = phys_of(t + 4);
     // a page-table entry outside [0, n_phys_pages) (uniform): its keys get no
     // weight, as the decode skips such a page
-    const bool tile_ok = ph_r >= 0;
-    store_tile(t, buf);
-    {
-      const uint32_t m1 = meta_next;
-      load_tile(t + 1, ph_a, m1);           // absent past the last tile
-    }
-    meta_next = load_meta(t + 2, ph_b);
-    ph_a = ph_b;
-    ph_b = ph_c;
+    const bool tile_ok = st.ph >= 0;
+    store_tile(t, buf, st);
+    load_tile(t + 2, ph_2, meta_2, st);     // absent past the last tile
+    ph_2 = ph_3;
+    meta_2 = meta_3;
+    ph_3 = ph_4;
     __syncthreads();
     const uint16_t* base = lds + buf * kTile;
 
@@ -456,7 +469,15 @@ __global__ __launch_bounds__(256, 2) void fact_prefill_kernel(FactPrefillParams 
       acc_c = mfma32(av, pb[sp], acc_c);
       acc_d = mfma32(ad, pb[sp], acc_d);
     }
+  };
+  // pairs of tiles, then an odd last one: no conditional step inside the
+  // loop, so the waits for each stage's loads see every load issued after it
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    tile_step(t, 0, sa);
+    tile_step(t + 1, 1, sb);
   }
+  if (t < n_tiles) tile_step(t, 0, sa);
 
   // ---- epilogue: bases of this KV head, transposed, into the page buffers
   __syncthreads();
